@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the bifocal-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch: the fused
+bifocal prefill of the prompt (g(s), on-the-fly correction, the three-pass
+merge) followed by one bifocal decode step of the next token against the
+resulting cache (split-K kernel + combine).  The default workload is the
+Qwen3-8B-shaped attention layer at 128K: batch 1, 32 query / 8 KV heads,
+head_dim 128, seq 131072, pretrained window 32768, local window 4096, RoPE base
+1e6 (g = 4), bf16 N(0,1) inputs from a fixed seed.
+
+Printed (one JSON line): prefill TFLOP/s on the algorithmic count
+4*D*Hq*B*s(s+1)/2 as ``value``; the roofline of the prefill kernel (bf16 MFMA
+peak 2.5 PFLOP/s); decode HBM GB/s over the K+V bytes (caches rotated so the
+256 MB last-level cache cannot hold them) and its overhead vs the plain decode
+built the same way; the plain causal prefill for comparison; and the fp64 CPU
+oracle timed on a bounded sample of rows.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bifocal prefill TFLOP/s @128K (% MFMA peak) + decode GB/s and overhead vs plain"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (workload id, batch, seq, Hq, Hkv, L, W, base)
+    "qwen3_8b_128k": (2, 1, 131072, 32, 8, 32768, 4096, 1e6),
+    "qwen3_1p7b_64k": (1, 1, 65536, 16, 8, 32768, 4096, 1e6),
+    "sweep_96k": (4, 1, 98304, 32, 8, 32768, 4096, 1e6),
+    "sweep_48k": (4, 1, 49152, 32, 8, 32768, 4096, 1e6),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(b, s, hq, d=128):
+    return 4.0 * d * hq * b * s * (s + 1) / 2.0
+
+
+def cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, n_rows, seed=0):
+    """Time the fp64 oracle on a bounded sample: n_rows random query rows of the
+    query heads of KV head 0; the rate is algorithmic FLOP/s of those rows."""
+    import oracle
+    from zero_shot_rope_attention_amd.inputs import bf16_bits_to_f64
+    s = qb.shape[1]
+    grp = hq // hkv
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(s, size=n_rows, replace=False))
+    q = bf16_bits_to_f64(qb[:, :, :grp])
+    k = bf16_bits_to_f64(kb[:, :, :1])
+    v = bf16_bits_to_f64(vb[:, :, :1])
+    t0 = time.perf_counter()
+    oracle.bifocal_three_pass(q, k, v, big_l, w, base, rows=rows, row_block=16)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * 128 * grp * float(np.sum(rows + 1))
+    threads = os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads) if threads else os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{n_rows} random query rows x {grp} query heads (KV head 0) of the workload, "
+                      f"fp64 numpy three-pass oracle, {dt:.1f} s; rate = algorithmic flops of those rows / time",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_8b_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--decode-iters", type=int, default=60)
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the plain-prefill and decode comparisons")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this library runs on one GPU (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import zero_shot_rope_attention_amd as jl
+    from zero_shot_rope_attention_amd.inputs import make_qkv
+
+    wid, b, s, hq, hkv, big_l, w, base = WORKLOADS[args.workload]
+    g = jl.jl_group_factor(s, big_l)
+    dev = torch.device("cuda:0")
+    log(f"workload {args.workload}: B={b} s={s} Hq={hq} Hkv={hkv} L={big_l} W={w} base={base} g={g}")
+
+    t0 = time.perf_counter()
+    qb, kb, vb = make_qkv(wid, b, s, s, hq, hkv, 128)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(qb), up(kb), up(vb)
+    log(f"inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    out = torch.empty_like(q)
+    lse = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
+    q_dec = q[:, -1:].contiguous()
+    out_dec = torch.empty_like(q_dec)
+    ws = torch.empty(jl.jl_bifocal_decode_workspace_size(b, s, hq, hkv), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        ev[0].record(stream)
+        jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
+        ev[1].record(stream)
+        jl.jl_bifocal_decode(q_dec, k, v, out_dec, None, big_l, w, base, ws)
+        ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warmup steps done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+    flops = prefill_flops(b, s, hq)
+    pre_avg = float(np.mean(pre_ms))
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    log(f"prefill {pre_avg:.2f} ms avg ({min(pre_ms):.2f} min) -> {tflops:.1f} TFLOP/s; step {ms_step:.2f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": b, "seq_len": s, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": 128, "pretrained_window": big_l, "local_window": w, "rope_base": base,
+                   "group_factor": g},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<bifocal>", "flops_per_launch": flops,
+                     "avg_launch_ms": round(pre_avg, 4)},
+        "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
+        "decode_in_step_us": round(float(np.mean(dec_ms)) * 1e3, 2),
+    }
+
+    if not args.no_extras:
+        # plain causal prefill built the same way (same numerator)
+        out_p = torch.empty_like(q)
+        for _ in range(2):
+            jl.jl_plain_prefill(q, k, v, out_p, None)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            jl.jl_plain_prefill(q, k, v, out_p, None)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        plain_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        result["plain_prefill"] = {"ms": round(plain_ms, 4),
+                                   "tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
+                                   "bifocal_over_plain_time": round(pre_avg / plain_ms, 4)}
+        log(f"plain prefill {plain_ms:.2f} ms")
+        del out_p
+
+        # decode: rotate among 3 caches (>= 1.5 GB at 128K) so the last-level cache cannot serve them;
+        # bifocal and plain interleaved.
+        caches = [(k, v)]
+        for r in range(2):
+            caches.append((k.clone(), v.clone()))
+        kv_bytes = 2 * b * s * hkv * 128 * 2
+        per = {"bifocal": [], "plain": []}
+        for it in range(args.decode_iters + 5):
+            for mode in ("bifocal", "plain"):
+                kc, vc = caches[it % len(caches)]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                if mode == "bifocal":
+                    jl.jl_bifocal_decode(q_dec, kc, vc, out_dec, None, big_l, w, base, ws)
+                else:
+                    jl.jl_plain_decode(q_dec, kc, vc, out_dec, None, ws)
+                e1.record(stream)
+                if it >= 5:
+                    per[mode].append((e0, e1))
+        torch.cuda.synchronize()
+        dec = {}
+        for mode, lst in per.items():
+            us = np.array([a.elapsed_time(bb) * 1e3 for a, bb in lst])
+            dec[mode] = {"us_median": round(float(np.median(us)), 2), "us_min": round(float(us.min()), 2),
+                         "GB_s": round(kv_bytes / (np.median(us) * 1e-6) / 1e9, 1)}
+        dec["kv_bytes"] = kv_bytes
+        dec["hbm_frac"] = round(dec["bifocal"]["GB_s"] / PEAK_HBM_GBS, 4)
+        dec["overhead_vs_plain"] = round(dec["bifocal"]["us_median"] / dec["plain"]["us_median"] - 1.0, 4)
+        dec["g"] = g
+        result["decode"] = dec
+        log(f"decode bifocal {dec['bifocal']['us_median']} us ({dec['bifocal']['GB_s']} GB/s), "
+            f"plain {dec['plain']['us_median']} us, overhead {dec['overhead_vs_plain'] * 100:.2f}%")
+        del caches
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * jl_bifocal.h -- C ABI of the MI355X (gfx950) bifocal-attention library.
+ *
+ * The operation is the attention of Jet-Long's Dynamic Bifocal RoPE
+ * (arXiv 2607.07740), as described by:
+ *   - ResearchPod summary (researchpod.app), 2nd paragraph: a local window that
+ *     keeps the original RoPE; a remote window whose positions are aliased by
+ *     the smallest integer grouping g that keeps remote rotation angles inside
+ *     the pretrained range; an inclusion-exclusion merge of three
+ *     FlashAttention passes fused into one kernel.
+ *   - ResearchPod transcript, exchange on the cache: the cache keeps the
+ *     original, uncompressed positions and the remapping correction is applied
+ *     at lookup time.
+ *   - ResearchPod transcript, exchange on prefill: the merge combines the local
+ *     view, the remapped distant view and a corrected version of the local view.
+ *   - Abstract (engineersofai.com paper page): exact recovery of the base model
+ *     at short inputs; inclusion-exclusion attention merge and an on-the-fly RoPE
+ *     correction rotation.
+ *   - seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap":
+ *     the long-range factor is computed from the current sequence length s.
+ *
+ * Definitions used by every entry point (head size D = 128):
+ *   s      = n_kv, the number of keys in context (cache index == position).
+ *   p_i    = n_kv - n_q + i, position of query row i (the newest n_q tokens).
+ *   theta_d= rope_base^(-2d/D), rotate-half pairs (d, d + D/2).
+ *   g      = jl_group_factor(s, L) = smallest integer >= 1 with
+ *            floor((s-1)/g) <= L-1  (== max(1, ceil(s/L))).
+ *   c(p)   = floor(p/g) - p (the correction rotation moves a vector cached at
+ *            position p to its aliased position floor(p/g)).
+ *   local  : 0 <= p_i - j <= W-1 (W keys including the query itself);
+ *   remote : j <= p_i - W.
+ *   Pass A = local keys, scores tau * q_i.k_j (base RoPE, as cached).
+ *   Pass B = all causal keys, scores tau * rot(q_i, c(p_i)th).rot(k_j, c(j)th).
+ *   Pass C = local keys, the scores of pass B.
+ *   out    = (w_A O_A + w_B O_B - w_C O_C) / (w_A + w_B - w_C), w_X = exp(lse_X - M).
+ *   tau    = softmax_scale, or 1/sqrt(D) when softmax_scale <= 0.
+ *
+ * Layout: every tensor is dense, row-major, "BSHD": q/out [B, n_q, Hq, D],
+ * k/v [B, n_kv, Hkv, D], element type bfloat16; lse is fp32 [B, Hq, n_q]
+ * (natural log).  Query head h reads KV head h / (Hq / Hkv).  Device pointers
+ * must be 16-byte aligned.
+ *
+ * Ownership and synchronisation: the caller owns every buffer.  The library
+ * never allocates or frees device memory and never synchronises the host;
+ * all work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ * default stream) and buffers must stay valid until the stream has finished.
+ * Device contents are not inspected on the host.
+ *
+ * Errors: every jl_status-returning call validates its host-visible arguments
+ * before touching the device.  On error nothing is enqueued, the status is
+ * returned and jl_last_error() holds a message (thread-local, valid until the
+ * next call on the same thread).  No call aborts or throws.
+ */
+#ifndef JL_BIFOCAL_H
+#define JL_BIFOCAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t jl_status;
+
+#define JL_OK              0
+#define JL_ERR_INVALID_ARG 1 /* null/misaligned pointer, size < 1, n_q > n_kv, Hq % Hkv != 0,
+                                L < 1, W < 1, W > L, rope_base <= 1 or not finite            */
+#define JL_ERR_UNSUPPORTED 2 /* head_dim != 128, or sizes whose element offsets overflow int64 */
+#define JL_ERR_WORKSPACE   3 /* decode workspace smaller than jl_bifocal_decode_workspace_size */
+#define JL_ERR_DEVICE      4 /* no HIP device, or a HIP error reported at launch              */
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* jl_last_error(void);
+
+/* g(s): smallest integer g >= 1 with floor((s-1)/g) <= L-1, i.e. every aliased
+ * position floor(p/g), p < s, falls inside the pretrained positions 0..L-1
+ * (ResearchPod summary, 2nd paragraph: "smallest integer grouping").
+ * Pure integer host function.  Returns 0 if seq_len < 1 or pretrained_window < 1. */
+int64_t jl_group_factor(int64_t seq_len, int64_t pretrained_window);
+
+/* Bifocal prefill (or a chunk of queries against a longer context).
+ *   q    : bf16 [B, n_q, Hq, D], rotated at positions p_i (as the model produced them)
+ *   k, v : bf16 [B, n_kv, Hkv, D], k rotated at its original positions 0..n_kv-1
+ *   out  : bf16 [B, n_q, Hq, D] (written)
+ *   lse  : fp32 [B, Hq, n_q] natural-log normaliser of the merged softmax, or NULL
+ * g = jl_group_factor(n_kv, L).  When g == 1 every remote rotation is the
+ * original one and the call runs jl_plain_prefill (bitwise identical results:
+ * the base model, Abstract "recovering the base model exactly").  Otherwise the
+ * fused kernel applies the correction rotation c(p) to q and k on the fly and
+ * evaluates the three-pass merge above.  Requires 1 <= W <= L. */
+jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                             int64_t local_window, double rope_base, float softmax_scale,
+                             void* stream);
+
+/* Plain causal RoPE attention built with the same kernel skeleton (the base
+ * model; denominator of the "overhead vs plain" and "vs plain causal"
+ * comparisons).  Same layouts as jl_bifocal_prefill. */
+jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, float softmax_scale, void* stream);
+
+/* Per-pass results of the three FlashAttention-style passes of the merge
+ * (ResearchPod transcript, prefill exchange: local view A, remapped distant
+ * view B, corrected local view C), each normalised on its own key set:
+ *   out_abc : fp32 [3, B, n_q, Hq, D]   (pass A, then B, then C)
+ *   lse_abc : fp32 [3, B, Hq, n_q]      natural log; -inf for an empty key set
+ * For checking and debugging; slower than jl_bifocal_prefill.  Runs the three
+ * passes for every g, including g == 1. */
+jl_status jl_bifocal_prefill_passes(const void* q, const void* k, const void* v, float* out_abc,
+                                    float* lse_abc, int32_t batch, int32_t n_q, int32_t n_kv,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int64_t pretrained_window, int64_t local_window,
+                                    double rope_base, float softmax_scale, void* stream);
+
+/* Bytes of device workspace jl_bifocal_decode / jl_plain_decode need for this
+ * shape (an upper bound over every L and W).  0 for invalid sizes. */
+size_t jl_bifocal_decode_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim);
+
+/* Bifocal decode: one new token per sequence against a cache that already holds
+ * its own key/value at position n_kv-1 (ResearchPod transcript, cache exchange:
+ * the cache keeps original positions; the correction is applied at lookup).
+ *   q              : bf16 [B, 1, Hq, D], rotated at position n_kv-1
+ *   k_cache/v_cache: bf16 [B, n_kv, Hkv, D], original positions, never modified
+ *   out            : bf16 [B, 1, Hq, D];  lse: fp32 [B, Hq, 1] or NULL
+ *   workspace      : device memory of at least jl_bifocal_decode_workspace_size bytes
+ *                    (16-byte aligned; contents on entry are ignored)
+ * g = jl_group_factor(n_kv, L).  The cache is split along its length into
+ * chunks that are wholly remote (grouped scores) or wholly local (base
+ * scores), reduced by a second kernel.  g == 1 runs jl_plain_decode. */
+jl_status jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                            float* lse, int32_t batch, int32_t n_kv, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                            int64_t local_window, double rope_base, float softmax_scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Plain decode with the same split-K kernels (no correction, no band). */
+jl_status jl_plain_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                          float* lse, int32_t batch, int32_t n_kv, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JL_BIFOCAL_H */

@@ -1,0 +1,92 @@
+"""GPU parity of the split-K bifocal decode against the fp64 oracle.
+
+The cache keeps original positions and is never rewritten (ResearchPod
+transcript, cache exchange), so one cache buffer serves every length: each call
+reads the first s positions, with the query at s - 1 and g = g(s), and must
+match the oracle at that s -- also across the pretrained window as g steps.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_shot_rope_attention_amd as jl
+from zero_shot_rope_attention_amd.inputs import bf16_bits_to_f64, make_qkv, normal_bf16
+
+from gpu_helpers import LSE_MEAN_TOL, LSE_TOL, assert_parity, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(q, kc, vc, s, big_l, w, base, plain=False):
+    b, _, hq, _ = q.shape
+    hkv = kc.shape[2]
+    out = torch.empty_like(q)
+    lse = torch.empty((b, hq, 1), dtype=torch.float32, device="cuda:0")
+    nbytes = jl.jl_bifocal_decode_workspace_size(b, s, hq, hkv)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    kk, vv = kc[:, :s], vc[:, :s]
+    print(f"decode s={s} B={b} Hq={hq} Hkv={hkv} L={big_l} W={w} plain={plain}", flush=True)
+    if plain:
+        jl.jl_plain_decode(q, kk, vv, out, lse, ws)
+    else:
+        jl.jl_bifocal_decode(q, kk, vv, out, lse, big_l, w, base, ws)
+    torch.cuda.synchronize()
+    return to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def test_decode_as_the_cache_grows():
+    big_l, w, base, n = 512, 128, 1e4, 2200
+    _, kb, vb = make_qkv(200, 1, 1, n, 4, 2, 128)
+    kc, vc = to_device(kb), to_device(vb)
+    kf, vf = bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+    for s in (1, 2, 127, 128, 129, 511, 512, 513, 600, 1024, 1025, 1536, 1537, 2048, 2200):
+        qb = normal_bf16(201, s, (1, 1, 4, 128))
+        q = to_device(qb)
+        out, lse = _decode(q, kc, vc, s, big_l, w, base)
+        ro, rl = oracle.bifocal_decode(bf16_bits_to_f64(qb), kf[:, :s], vf[:, :s], big_l, w, base)
+        assert_parity(out, ro, f"decode s={s} (g={oracle.group_factor(s, big_l)})")
+        assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+
+
+@pytest.mark.parametrize("n_kv", [32768, 65536, 131072])
+def test_decode_workload_sizes(n_kv):
+    # one query, 32 query heads / 8 KV heads, D 128, L 32768, W 4096, base 1e6
+    qb = normal_bf16(210, 0, (1, 1, 32, 128))
+    kb = normal_bf16(210, 1, (1, n_kv, 8, 128))
+    vb = normal_bf16(210, 2, (1, n_kv, 8, 128))
+    out, lse = _decode(to_device(qb), to_device(kb), to_device(vb), n_kv, 32768, 4096, 1e6)
+    ro, rl = oracle.bifocal_decode(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb), 32768, 4096,
+                                   1e6)
+    assert_parity(out, ro, f"decode {n_kv}")
+    assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+
+
+def test_decode_g1_is_plain_bitwise_and_batched():
+    qb, kb, vb = make_qkv(220, 2, 1, 3000, 8, 2, 128)
+    q, kc, vc = to_device(qb), to_device(kb), to_device(vb)
+    out, lse = _decode(q, kc, vc, 3000, 4096, 512, 1e6)
+    out_p, lse_p = _decode(q, kc, vc, 3000, 4096, 512, 1e6, plain=True)
+    assert np.array_equal(out, out_p) and np.array_equal(lse, lse_p)
+    ro, rl = oracle.plain_causal_attention(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb))
+    assert_parity(out, ro)
+    assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+
+
+def test_decode_batched_bifocal_max_group():
+    # batch 2, 16 query heads per KV head (the largest group the decode takes)
+    qb, kb, vb = make_qkv(221, 2, 1, 1500, 32, 2, 128)
+    out, lse = _decode(to_device(qb), to_device(kb), to_device(vb), 1500, 400, 100, 1e4)
+    ro, rl = oracle.bifocal_decode(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb), 400, 100, 1e4)
+    assert_parity(out, ro)
+    assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+
+
+def test_decode_matches_last_prefill_row():
+    qb, kb, vb = make_qkv(222, 1, 700, 700, 4, 2, 128)
+    q, kc, vc = to_device(qb), to_device(kb), to_device(vb)
+    out = torch.empty_like(q)
+    jl.jl_bifocal_prefill(q, kc, vc, out, None, 200, 50, 1e4)
+    dec, _ = _decode(q[:, -1:].contiguous(), kc, vc, 700, 200, 50, 1e4)
+    assert_parity(dec, to_f64(out[:, -1:]), "decode vs prefill last row", max_tol=1e-2, mean_tol=1e-3)

@@ -1,0 +1,150 @@
+"""Python binding of the MI355X bifocal-attention library (``libjetlong.so``).
+
+Argument marshalling only: every function here takes torch tensors that the
+caller has allocated on the GPU, passes their device pointers, sizes and the
+current HIP stream to the C ABI of the same name (``include/jl_bifocal.h``),
+and raises :class:`JetLongError` on a non-zero status.  All computation runs in
+the library's HIP kernels; there is no fallback.  The library is loaded on
+first use and must have been built (``zero_shot_rope_attention_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "JetLongError",
+    "LIB_PATH",
+    "EXPORTED_SYMBOLS",
+    "load_library",
+    "jl_group_factor",
+    "jl_bifocal_prefill",
+    "jl_plain_prefill",
+    "jl_bifocal_prefill_passes",
+    "jl_bifocal_decode_workspace_size",
+    "jl_bifocal_decode",
+    "jl_plain_decode",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
+
+_i32, _i64, _f32, _f64, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double,
+                                    ctypes.c_void_p, ctypes.c_size_t)
+
+# name -> (restype, argtypes); must match include/jl_bifocal.h
+_SIGNATURES = {
+    "jl_last_error": (ctypes.c_char_p, []),
+    "jl_group_factor": (_i64, [_i64, _i64]),
+    "jl_bifocal_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
+                                  _f32, _vp]),
+    "jl_plain_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "jl_bifocal_prefill_passes": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                         _f64, _f32, _vp]),
+    "jl_bifocal_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "jl_bifocal_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64, _f32,
+                                 _vp, _sz, _vp]),
+    "jl_plain_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_STATUS = {1: "JL_ERR_INVALID_ARG", 2: "JL_ERR_UNSUPPORTED", 3: "JL_ERR_WORKSPACE", 4: "JL_ERR_DEVICE"}
+_lib = None
+
+
+class JetLongError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libjetlong.so (once) and declare its C signatures.  Raises if it has
+    not been built: there is no fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m zero_shot_rope_attention_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().jl_last_error()
+        raise JetLongError(status, msg.decode() if msg else "")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous device tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def jl_group_factor(seq_len: int, pretrained_window: int) -> int:
+    return int(load_library().jl_group_factor(int(seq_len), int(pretrained_window)))
+
+
+def jl_bifocal_prefill(q, k, v, out, lse, pretrained_window, local_window, rope_base,
+                       softmax_scale=0.0, stream=None):
+    """q [B, n_q, Hq, D], k/v [B, n_kv, Hkv, D] bf16; out like q; lse fp32 [B, Hq, n_q] or None."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    _check(load_library().jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq,
+                                             hkv, d, int(pretrained_window), int(local_window), float(rope_base),
+                                             float(softmax_scale), _stream(stream)))
+
+
+def jl_plain_prefill(q, k, v, out, lse, softmax_scale=0.0, stream=None):
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    _check(load_library().jl_plain_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq, hkv,
+                                           d, float(softmax_scale), _stream(stream)))
+
+
+def jl_bifocal_prefill_passes(q, k, v, out_abc, lse_abc, pretrained_window, local_window, rope_base,
+                              softmax_scale=0.0, stream=None):
+    """out_abc fp32 [3, B, n_q, Hq, D]; lse_abc fp32 [3, B, Hq, n_q]."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    _check(load_library().jl_bifocal_prefill_passes(_ptr(q), _ptr(k), _ptr(v), _ptr(out_abc), _ptr(lse_abc), b, n_q,
+                                                    n_kv, hq, hkv, d, int(pretrained_window), int(local_window),
+                                                    float(rope_base), float(softmax_scale), _stream(stream)))
+
+
+def jl_bifocal_decode_workspace_size(batch, n_kv, n_q_heads, n_kv_heads, head_dim=128) -> int:
+    return int(load_library().jl_bifocal_decode_workspace_size(batch, n_kv, n_q_heads, n_kv_heads, head_dim))
+
+
+def jl_bifocal_decode(q, k_cache, v_cache, out, lse, pretrained_window, local_window, rope_base, workspace,
+                      softmax_scale=0.0, stream=None):
+    """q [B, 1, Hq, D]; caches [B, n_kv, Hkv, D]; workspace: a device tensor of
+    at least jl_bifocal_decode_workspace_size bytes."""
+    b, _, hq, d = q.shape
+    n_kv, hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b, n_kv,
+                                            hq, hkv, d, int(pretrained_window), int(local_window), float(rope_base),
+                                            float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_plain_decode(q, k_cache, v_cache, out, lse, workspace, softmax_scale=0.0, stream=None):
+    b, _, hq, d = q.shape
+    n_kv, hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_plain_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b, n_kv, hq,
+                                          hkv, d, float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))

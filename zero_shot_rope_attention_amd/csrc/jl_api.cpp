@@ -1,0 +1,229 @@
+// C ABI of the bifocal-attention library: argument validation, g(s), launch
+// planning and error reporting.  Declarations and contracts: include/jl_bifocal.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "jl_bifocal.h"
+#include "jl_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+jl_status fail(jl_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+jl_status ok() {
+  g_err[0] = '\0';
+  return JL_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Elements of a [b, n, h, 128] tensor, or -1 on int64 overflow.
+int64_t elements(int64_t b, int64_t n, int64_t h) {
+  const int64_t lim = INT64_C(1) << 55;
+  if (b > lim / n) return -1;
+  int64_t x = b * n;
+  if (x > lim / h) return -1;
+  x *= h;
+  if (x > lim / 128) return -1;
+  return x * 128;
+}
+
+// One query of the HIP runtime per process: is there a usable device?
+jl_status device_check() {
+  static int state = -1;  // -1 unknown, 0 none, 1 present
+  if (state < 0) {
+    int count = 0;
+    state = (hipGetDeviceCount(&count) == hipSuccess && count > 0) ? 1 : 0;
+  }
+  if (state == 0) return fail(JL_ERR_DEVICE, "no HIP device available");
+  return JL_OK;
+}
+
+jl_status check_pointer(const void* p, const char* name, bool nullable = false) {
+  if (!p) return nullable ? JL_OK : fail(JL_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(JL_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return JL_OK;
+}
+
+struct Shape {
+  int32_t batch, n_q, n_kv, hq, hkv, head_dim;
+};
+
+jl_status check_shape(const Shape& s) {
+  if (s.batch < 1 || s.n_q < 1 || s.n_kv < 1 || s.hq < 1 || s.hkv < 1 || s.head_dim < 1)
+    return fail(JL_ERR_INVALID_ARG, "sizes must be >= 1 (batch=%d n_q=%d n_kv=%d Hq=%d Hkv=%d D=%d)", s.batch,
+                s.n_q, s.n_kv, s.hq, s.hkv, s.head_dim);
+  if (s.n_q > s.n_kv) return fail(JL_ERR_INVALID_ARG, "n_q (%d) > n_kv (%d)", s.n_q, s.n_kv);
+  if (s.hq % s.hkv) return fail(JL_ERR_INVALID_ARG, "n_q_heads (%d) %% n_kv_heads (%d) != 0", s.hq, s.hkv);
+  if (s.head_dim != 128) return fail(JL_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", s.head_dim);
+  if (elements(s.batch, s.n_q, s.hq) < 0 || elements(s.batch, s.n_kv, s.hkv) < 0)
+    return fail(JL_ERR_UNSUPPORTED, "tensor sizes overflow 64-bit element offsets");
+  return JL_OK;
+}
+
+jl_status check_windows(int64_t big_l, int64_t w, double base) {
+  if (big_l < 1) return fail(JL_ERR_INVALID_ARG, "pretrained_window must be >= 1 (got %lld)", (long long)big_l);
+  if (w < 1) return fail(JL_ERR_INVALID_ARG, "local_window must be >= 1 (got %lld)", (long long)w);
+  if (w > big_l)
+    return fail(JL_ERR_INVALID_ARG, "local_window (%lld) > pretrained_window (%lld)", (long long)w,
+                (long long)big_l);
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(JL_ERR_INVALID_ARG, "rope_base must be finite and > 1");
+  return JL_OK;
+}
+
+jl_status check_scale(float scale, float* out) {
+  if (std::isnan(scale) || std::isinf(scale)) return fail(JL_ERR_INVALID_ARG, "softmax_scale is not finite");
+  *out = scale > 0.0f ? scale : 1.0f / std::sqrt(128.0f);
+  return JL_OK;
+}
+
+jl_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(JL_ERR_DEVICE, "HIP launch error: %s", hipGetErrorString(e));
+  return ok();
+}
+
+#define JL_TRY(expr)                \
+  do {                              \
+    jl_status st_ = (expr);         \
+    if (st_ != JL_OK) return st_;   \
+  } while (0)
+
+jl_status prefill_common(const void* q, const void* k, const void* v, const Shape& s, float scale_in,
+                         float* scale) {
+  JL_TRY(check_pointer(q, "q"));
+  JL_TRY(check_pointer(k, "k"));
+  JL_TRY(check_pointer(v, "v"));
+  JL_TRY(check_shape(s));
+  JL_TRY(check_scale(scale_in, scale));
+  return JL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* jl_last_error(void) { return g_err; }
+
+int64_t jl_group_factor(int64_t seq_len, int64_t pretrained_window) {
+  if (seq_len < 1 || pretrained_window < 1) return 0;
+  // smallest g with (s - 1) / g <= L - 1  <=>  s <= g L  <=>  g = ceil(s / L)
+  const int64_t g = seq_len / pretrained_window + (seq_len % pretrained_window != 0);
+  return g < 1 ? 1 : g;
+}
+
+jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
+                           int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           float softmax_scale, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(device_check());
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, 1, 2.0,
+                       scale};
+  return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
+                             int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                             int64_t pretrained_window, int64_t local_window, double rope_base,
+                             float softmax_scale, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(device_check());
+  const int64_t g = jl_group_factor(n_kv, pretrained_window);
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  const jl::PrefillMode mode = g == 1 ? jl::kModePlain : jl::kModeBifocal;
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, (int32_t)g, w,
+                       rope_base, scale};
+  return launched(jl::launch_prefill(mode, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_bifocal_prefill_passes(const void* q, const void* k, const void* v, float* out_abc, float* lse_abc,
+                                    int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                    int64_t local_window, double rope_base, float softmax_scale, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out_abc, "out_abc"));
+  JL_TRY(check_pointer(lse_abc, "lse_abc"));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(device_check());
+  const int64_t g = jl_group_factor(n_kv, pretrained_window);
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  jl::PrefillProblem p{q, k, v, nullptr, nullptr, out_abc, lse_abc, batch, n_q, n_kv, n_q_heads, n_kv_heads,
+                       (int32_t)g, w, rope_base, scale};
+  return launched(jl::launch_prefill(jl::kModePasses, p, static_cast<hipStream_t>(stream)));
+}
+
+size_t jl_bifocal_decode_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim) {
+  if (batch < 1 || n_kv < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim != 128) return 0;
+  return jl::decode_workspace_bytes(batch, n_kv, n_q_heads);
+}
+
+static jl_status decode_common(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& s,
+                               float scale_in, float* scale, void* workspace, size_t workspace_bytes) {
+  JL_TRY(check_pointer(q, "q"));
+  JL_TRY(check_pointer(k, "k_cache"));
+  JL_TRY(check_pointer(v, "v_cache"));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_shape(s));
+  if (s.hq / s.hkv > 16)
+    return fail(JL_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", s.hq / s.hkv);
+  JL_TRY(check_scale(scale_in, scale));
+  JL_TRY(check_pointer(workspace, "workspace"));
+  const size_t need = jl::decode_workspace_bytes(s.batch, s.n_kv, s.hq);
+  if (workspace_bytes < need)
+    return fail(JL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
+                need);
+  return JL_OK;
+}
+
+jl_status jl_plain_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                          int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                          float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  JL_TRY(device_check());
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, batch, n_kv, n_q_heads, n_kv_heads, 1, 0, 2.0, scale, workspace};
+  return launched(jl::launch_decode(false, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                            int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int64_t pretrained_window, int64_t local_window, double rope_base, float softmax_scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(device_check());
+  const int64_t g = jl_group_factor(n_kv, pretrained_window);
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, batch, n_kv, n_q_heads, n_kv_heads, (int32_t)g, w, rope_base,
+                      scale, workspace};
+  return launched(jl::launch_decode(g > 1, p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

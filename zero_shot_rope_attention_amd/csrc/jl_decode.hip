@@ -1,0 +1,371 @@
+// Split-K bifocal decode for gfx950 (MI355X): one new query per sequence
+// against a KV cache that keeps original positions (ResearchPod transcript,
+// cache exchange: the cache is never rewritten; the correction is applied at
+// lookup).
+//
+// At one query (position p = s - 1) the local keys are the contiguous suffix
+// [s - W, s) and the remote keys the prefix [0, s - W).  Pass B minus pass C of
+// the inclusion-exclusion merge then covers exactly the remote prefix with
+// grouped scores, and pass A the local suffix with base scores, so the merged
+// softmax is the combination of two disjoint partial softmaxes.  The cache is
+// cut into chunks that never straddle s - W; every chunk yields a partial
+// (normalised output, log-sum-exp) and a second kernel merges the partials.
+//
+// Per workgroup: one KV head, its G query heads, one chunk of up to 512 keys
+// (4 waves x 128 keys).  Per wave and 32-key block:
+//   S^T = K Q^T   (MFMA; A = key fragments loaded straight from HBM, 16-byte
+//                  loads; remote keys are rotated by c(j) theta in registers,
+//                  each lane holding both halves of its rotate-half pairs)
+//   O^T += V^T P^T (MFMA; V transposed through a per-wave LDS tile)
+#include <cmath>
+
+#include "jl_device.h"
+#include "jl_launch.h"
+
+namespace jl {
+namespace {
+
+constexpr int kKeysPerWave = 128;
+constexpr int kWaves = 4;
+constexpr int kKeysPerWG = kKeysPerWave * kWaves;
+constexpr int kMaxGroup = 16;  // query heads per KV head handled by one workgroup
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;
+  float* part_o;    // [B, Hq, n_wg, D]
+  float* part_lse;  // [B, Hq, n_wg]
+  int32_t batch, n_kv, hq, hkv, grp;
+  int32_t g;
+  int32_t remote_end;  // keys [0, remote_end) are remote (grouped scores)
+  int32_t n_rem_wg;    // chunks covering the remote prefix
+  int32_t n_wg;        // total chunks
+  float inv_g;
+  float scale_log2;
+  float theta_rev32[kHalfD];
+  double theta_rev[kHalfD];
+};
+
+__device__ __forceinline__ int perm_key(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+__device__ __forceinline__ float elem(const u32x4& u, int e) {
+  uint32_t w = u[e >> 1];
+  return (e & 1) ? bf_hi(w) : bf_lo(w);
+}
+
+// transposed V tile of one wave: [128 d][32 keys] bf16, 64-byte rows, swizzled
+__device__ __forceinline__ int vt_off(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
+
+template <bool BIF>
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kWaves][kD * 32 * 2];
+  __shared__ float s_m[kWaves][kMaxGroup];
+  __shared__ float s_l[kWaves][kMaxGroup];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int n = lane & 31;
+  const int sp = blockIdx.x;
+  const int b = blockIdx.y / a.hkv;
+  const int kvh = blockIdx.y % a.hkv;
+
+  int ks, ke;
+  bool remote = false;
+  if (sp < a.n_rem_wg) {
+    ks = sp * kKeysPerWG;
+    ke = min(a.remote_end, ks + kKeysPerWG);
+    remote = BIF;
+  } else {
+    ks = a.remote_end + (sp - a.n_rem_wg) * kKeysPerWG;
+    ke = min(a.n_kv, ks + kKeysPerWG);
+  }
+  const int ws = ks + wave * kKeysPerWave;
+  const int we = min(ke, ws + kKeysPerWave);
+
+  const int64_t kv_rs = (int64_t)a.hkv * kD;
+  const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+  const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+
+  // query fragment (B operand of S^T): column n = query head kvh*G + n (n < G)
+  bf16x8 qf[8];
+  {
+    const bool col_ok = n < a.grp;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.hq + kvh * a.grp + (col_ok ? n : 0)) * kD;
+    u32x4 raw[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      raw[kk] = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
+    if (remote) {
+      const int p = a.n_kv - 1;
+      const long long cq = (long long)(p / a.g) - p;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 lo, hi;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int e = 2 * e2 + t;
+            const f32x2 cs = rot_cs(cq, a.theta_rev[16 * kk + 8 * h + e]);
+            const float x1 = elem(raw[kk], e), x2 = elem(raw[kk + 4], e);
+            y1[t] = x1 * cs.x - x2 * cs.y;
+            y2[t] = x2 * cs.x + x1 * cs.y;
+          }
+          lo[e2] = pack_bf16(y1[0], y1[1]);
+          hi[e2] = pack_bf16(y2[0], y2[1]);
+        }
+        raw[kk] = lo;
+        raw[kk + 4] = hi;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(raw[kk]);
+  }
+
+  // Remote keys: c(j) = c(ws) - u(j), u = t - floor((r + t)/g), t = j - ws,
+  // r = ws mod g.  The angle c(ws) theta_d is reduced in fp64 once per wave;
+  // the small per-key part u theta_d (u < 128) is exact enough in fp32.
+  float fb[4][8], th[4][8];
+  int r_s = 0;
+  if (BIF && remote) {
+    const long long cb = (long long)(ws / a.g) - ws;
+    r_s = ws % a.g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * kk + 8 * h + e;
+        const double r = (double)cb * a.theta_rev[d];
+        fb[kk][e] = (float)(r - __builtin_rint(r));
+        th[kk][e] = a.theta_rev32[d];
+      }
+  }
+
+  float m_run = kNegBig, l_run = 0.0f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x16{};
+  uint8_t* vt = s_vt[wave];
+
+  for (int j0 = ws; j0 < we; j0 += 32) {
+    // ---- key fragment for key j0 + perm_key(n), d = 16kk + 8h + e ----
+    const int jk = j0 + perm_key(n);
+    const bool k_ok = jk < we;
+    u32x4 kr[8];
+    {
+      const uint16_t* kp = kbase + (int64_t)(k_ok ? jk : ws) * kv_rs + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        kr[kk] = k_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * kk) : u32x4{0, 0, 0, 0};
+    }
+    // ---- V rows for the transposed LDS tile: items (4 keys, 8-d chunk) ----
+    u32x4 vr[2][4];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int item = lane + 64 * it;
+      const int kg = item >> 4, dc = item & 15;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int j = j0 + 4 * kg + q4;
+        vr[it][q4] = (j < we) ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * kv_rs + 8 * dc)
+                              : u32x4{0, 0, 0, 0};
+      }
+    }
+    if (BIF && remote) {
+      const int t = jk - ws;
+      const int u = t - small_div(r_s + t, a.g, a.inv_g);
+      const float uf = (float)u;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 lo, hi;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int e = 2 * e2 + q2;
+            const float rev = fb[kk][e] - uf * th[kk][e];  // angle in revolutions
+            const float co = __builtin_amdgcn_cosf(rev);
+            const float si = __builtin_amdgcn_sinf(rev);
+            const float x1 = elem(kr[kk], e), x2 = elem(kr[kk + 4], e);
+            y1[q2] = x1 * co - x2 * si;
+            y2[q2] = x2 * co + x1 * si;
+          }
+          lo[e2] = pack_bf16(y1[0], y1[1]);
+          hi[e2] = pack_bf16(y2[0], y2[1]);
+        }
+        kr[kk] = lo;
+        kr[kk + 4] = hi;
+      }
+    }
+    f32x16 s = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = mfma32(as_bf16x8(kr[kk]), qf[kk], s);
+
+    // ---- online softmax: lane holds head n, keys j0 + 16h + i ----
+    float x[16];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = (j0 + 16 * h + i < we) ? s[i] * a.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, x[i]);
+    }
+    mloc = fmaxf(mloc, swap_halves(mloc));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    uint32_t pk[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i2 = 0; i2 < 8; ++i2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[2 * i2] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(x[2 * i2 + 1] - m_new);
+      psum += p0 + p1;
+      pk[i2] = pack_bf16(p0, p1);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
+
+    // ---- V^T tile: for each d, 4 consecutive keys -> one 8-byte LDS store ----
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int item = lane + 64 * it;
+      const int kg = item >> 4, dc = item & 15;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        const uint32_t v0 = (vr[it][0][e >> 1] >> sh) & 0xffffu, v1 = (vr[it][1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t v2 = (vr[it][2][e >> 1] >> sh) & 0xffffu, v3 = (vr[it][3][e >> 1] >> sh) & 0xffffu;
+        const int d = 8 * dc + e;
+        *reinterpret_cast<u32x2*>(vt + vt_off(d, kg >> 1) + ((kg & 1) << 3)) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const u32x4 pf = {pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]};
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + vt_off(32 * nb + n, 2 * h + half));
+        acc[nb] = mfma32(as_bf16x8(vf), as_bf16x8(pf), acc[nb]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the four waves' partial softmaxes of this chunk ----
+  const float lt = l_run + swap_halves(l_run);
+  __syncthreads();  // every wave is done with its V^T tile
+  float* red = reinterpret_cast<float*>(&s_vt[0][0]);  // [wave][G][D] fp32
+  if (n < a.grp) {
+    if (h == 0) {
+      s_m[wave][n] = m_run;
+      s_l[wave][n] = lt;
+    }
+    float* dst = red + ((size_t)wave * a.grp + n) * kD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(dst + 32 * nb + 8 * i4 + 4 * h) =
+            float4{acc[nb][4 * i4], acc[nb][4 * i4 + 1], acc[nb][4 * i4 + 2], acc[nb][4 * i4 + 3]};
+  }
+  __syncthreads();
+  for (int item = tid; item < a.grp * kD; item += kWaves * 64) {
+    const int hh = item / kD, d = item % kD;
+    float mx = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][hh]);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = __builtin_amdgcn_exp2f(s_m[w][hh] - mx);
+      lsum += s_l[w][hh] * sc;
+      o += red[((size_t)w * a.grp + hh) * kD + d] * sc;
+    }
+    const int64_t bh = (int64_t)b * a.hq + kvh * a.grp + hh;
+    a.part_o[(bh * a.n_wg + sp) * kD + d] = o / lsum;
+    if (d == 0) a.part_lse[bh * a.n_wg + sp] = (mx + __builtin_log2f(lsum)) * kLn2;
+  }
+}
+
+// Merge the per-chunk partials of one (sequence, query head): lse-weighted sum.
+__global__ __launch_bounds__(kD) void decode_combine_kernel(const float* part_o, const float* part_lse, uint16_t* out,
+                                                            float* lse, int n_wg) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* pl = part_lse + bh * n_wg;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_wg; ++s) mx = fmaxf(mx, pl[s]);
+  float wsum = 0.0f, o = 0.0f;
+  for (int s = 0; s < n_wg; ++s) {
+    const float w = __expf(pl[s] - mx);
+    wsum += w;
+    o += w * part_o[(bh * n_wg + s) * kD + d];
+  }
+  const float r = o / wsum;
+  f32x2 f = {r, 0.0f};
+  const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  out[bh * kD + d] = (uint16_t)(pk & 0xffffu);
+  if (lse && d == 0) lse[bh] = mx + __logf(wsum);
+}
+
+}  // namespace
+
+int32_t decode_max_splits(int32_t n_kv) { return (n_kv + kKeysPerWG - 1) / kKeysPerWG + 1; }
+
+size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads) {
+  const size_t rows = (size_t)batch * n_q_heads * decode_max_splits(n_kv);
+  return rows * kD * sizeof(float) + rows * sizeof(float);
+}
+
+hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t stream) {
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.out = static_cast<uint16_t*>(p.out);
+  a.lse = p.lse;
+  a.batch = p.batch;
+  a.n_kv = p.n_kv;
+  a.hq = p.n_q_heads;
+  a.hkv = p.n_kv_heads;
+  a.grp = p.n_q_heads / p.n_kv_heads;
+  if (a.grp > kMaxGroup) return hipErrorInvalidValue;
+  a.g = bifocal ? p.group : 1;
+  a.remote_end = bifocal ? p.n_kv - p.local_window : 0;
+  if (a.remote_end < 0) a.remote_end = 0;
+  a.n_rem_wg = (a.remote_end + kKeysPerWG - 1) / kKeysPerWG;
+  a.n_wg = a.n_rem_wg + (p.n_kv - a.remote_end + kKeysPerWG - 1) / kKeysPerWG;
+  a.inv_g = 1.0f / (float)a.g;
+  a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int d = 0; d < kHalfD; ++d) {
+    a.theta_rev[d] = std::pow(p.rope_base, -2.0 * d / kD) / two_pi;
+    a.theta_rev32[d] = (float)a.theta_rev[d];
+  }
+  const size_t rows = (size_t)p.batch * p.n_q_heads * decode_max_splits(p.n_kv);
+  a.part_o = static_cast<float*>(p.workspace);
+  a.part_lse = a.part_o + rows * kD;
+  // partials are laid out with the actual chunk count as the row stride
+  if (bifocal)
+    hipLaunchKernelGGL((decode_split_kernel<true>), dim3(a.n_wg, p.batch * p.n_kv_heads), dim3(kWaves * 64), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<false>), dim3(a.n_wg, p.batch * p.n_kv_heads), dim3(kWaves * 64), 0,
+                       stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kD), 0, stream, a.part_o, a.part_lse,
+                     a.out, a.lse, a.n_wg);
+  return hipGetLastError();
+}
+
+}  // namespace jl

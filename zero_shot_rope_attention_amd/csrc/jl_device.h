@@ -1,0 +1,77 @@
+// Device-side building blocks shared by the prefill and decode kernels (gfx950).
+//
+// Matrix products use v_mfma_f32_32x32x16_bf16 (32x32 output tile, K = 16 per
+// instruction).  Lane layout of that instruction on a 64-wide wave, with
+// h = lane / 32 and n = lane % 32:
+//   A (32 x 16): lane holds A[n][8h + e], e = 0..7
+//   B (16 x 32): lane holds B[8h + e][n], e = 0..7
+//   D (32 x 32): lane holds D[8(i/4) + 4h + (i%4)][n], i = 0..15
+// Only the pairing of A's and B's k index matters for the sum, so the kernels
+// are free to choose which key each k index stands for.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;     // head size
+constexpr int kHalfD = 64;  // rotate-half pairs (d, d + 64)
+constexpr int kBN = 64;     // keys per tile
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// bf16 halves of a packed dword -> fp32
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// cos/sin of the angle c * theta_d, where theta_rev = theta_d / (2 pi).
+// The product is reduced to [-1/2, 1/2] revolutions in fp64 (|c| theta_d can
+// reach ~1e5 rad, where an fp32 angle would already be off by ~1e-2 rad), then
+// evaluated in fp32.
+__device__ __forceinline__ f32x2 rot_cs(long long c, double theta_rev) {
+  double r = (double)c * theta_rev;
+  double f = r - __builtin_rint(r);
+  float a = (float)(f * 6.283185307179586476925286766559);
+  float s, co;
+  sincosf(a, &s, &co);
+  return f32x2{co, s};
+}
+
+// Complex product (a.x + i a.y)(b.x + i b.y).
+__device__ __forceinline__ f32x2 cmul(f32x2 a, f32x2 b) {
+  return f32x2{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x};
+}
+
+// Wave-wide exchange with the lane 32 positions away (the other half-wave).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// floor(n / g) for 0 <= n < 2^22 and 1 <= g, using a float reciprocal plus an
+// exact integer correction.
+__device__ __forceinline__ int small_div(int n, int g, float inv_g) {
+  int q = (int)((float)n * inv_g);
+  if ((q + 1) * g <= n) ++q;
+  if (q * g > n) --q;
+  return q;
+}
+
+}  // namespace jl

@@ -1,0 +1,51 @@
+// Host-side launch interface between the C ABI (jl_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jl {
+
+enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2 };
+
+// Everything a prefill launch needs; validated by the caller.
+struct PrefillProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;        // bf16 [B, n_q, Hq, D]       (plain / bifocal)
+  float* lse;       // fp32 [B, Hq, n_q] or null  (plain / bifocal)
+  float* out_abc;   // fp32 [3, B, n_q, Hq, D]    (passes)
+  float* lse_abc;   // fp32 [3, B, Hq, n_q]       (passes)
+  int32_t batch, n_q, n_kv, n_q_heads, n_kv_heads;
+  int32_t group;         // g(s); 1 for plain
+  int32_t local_window;  // W, already clamped to <= n_kv
+  double rope_base;
+  float softmax_scale;   // > 0
+};
+
+hipError_t launch_prefill(PrefillMode mode, const PrefillProblem& p, hipStream_t stream);
+
+struct DecodeProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int32_t batch, n_kv, n_q_heads, n_kv_heads;
+  int32_t group;         // g(s); 1 for plain
+  int32_t local_window;  // W clamped to <= n_kv; 0 for plain (no local/remote split)
+  double rope_base;
+  float softmax_scale;
+  void* workspace;
+};
+
+// Number of key chunks the decode splits a cache of n_kv keys into (upper bound
+// over every local window), and the workspace bytes that many chunks need.
+int32_t decode_max_splits(int32_t n_kv);
+size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads);
+
+hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t stream);
+
+}  // namespace jl
