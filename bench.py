@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3_8b_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-iters", type=int, default=60)
-    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the plain-prefill and decode comparisons")
     args = ap.parse_args()

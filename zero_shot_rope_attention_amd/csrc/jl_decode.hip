@@ -297,24 +297,58 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
 }
 
 // Merge the per-chunk partials of one (sequence, query head): lse-weighted sum.
-__global__ __launch_bounds__(kD) void decode_combine_kernel(const float* part_o, const float* part_lse, uint16_t* out,
-                                                            float* lse, int n_wg) {
+// 256 threads: 8 groups of 32 threads; a group walks every 8th chunk, each of
+// its threads owning 4 of the 128 output columns (one 512-byte row per step).
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* part_o, const float* part_lse,
+                                                                         uint16_t* out, float* lse, int n_wg) {
+  __shared__ float s_red[kCombineThreads / 64];
+  __shared__ float4 s_acc[8][32];
+  __shared__ float s_w[8];
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const float* pl = part_lse + bh * n_wg;
+  // maximum over chunks
   float mx = -INFINITY;
-  for (int s = 0; s < n_wg; ++s) mx = fmaxf(mx, pl[s]);
-  float wsum = 0.0f, o = 0.0f;
-  for (int s = 0; s < n_wg; ++s) {
+  for (int s = tid; s < n_wg; s += kCombineThreads) mx = fmaxf(mx, pl[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  // weighted sum
+  const int grp = tid >> 5, c4 = tid & 31;
+  float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  float wsum = 0.0f;
+  for (int s = grp; s < n_wg; s += 8) {
     const float w = __expf(pl[s] - mx);
+    const float4 x = *reinterpret_cast<const float4*>(part_o + (bh * n_wg + s) * kD + 4 * c4);
+    o.x += w * x.x;
+    o.y += w * x.y;
+    o.z += w * x.z;
+    o.w += w * x.w;
     wsum += w;
-    o += w * part_o[(bh * n_wg + s) * kD + d];
   }
-  const float r = o / wsum;
-  f32x2 f = {r, 0.0f};
-  const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-  out[bh * kD + d] = (uint16_t)(pk & 0xffffu);
-  if (lse && d == 0) lse[bh] = mx + __logf(wsum);
+  s_acc[grp][c4] = o;
+  if (c4 == 0) s_w[grp] = wsum;
+  __syncthreads();
+  if (tid < 32) {
+    float4 t = s_acc[0][tid];
+    float ws = s_w[0];
+#pragma unroll
+    for (int gi = 1; gi < 8; ++gi) {
+      const float4 x = s_acc[gi][tid];
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+      ws += s_w[gi];
+    }
+    const float inv = 1.0f / ws;
+    const u32x2 pk = {pack_bf16(t.x * inv, t.y * inv), pack_bf16(t.z * inv, t.w * inv)};
+    *reinterpret_cast<u32x2*>(out + bh * kD + 4 * tid) = pk;
+    if (lse && tid == 0) lse[bh] = mx + __logf(ws);
+  }
 }
 
 }  // namespace
@@ -363,7 +397,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kD), 0, stream, a.part_o, a.part_lse,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kCombineThreads), 0, stream, a.part_o, a.part_lse,
                      a.out, a.lse, a.n_wg);
   return hipGetLastError();
 }

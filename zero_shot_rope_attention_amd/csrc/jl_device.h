@@ -46,20 +46,37 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // cos/sin of the angle c * theta_d, where theta_rev = theta_d / (2 pi).
 // The product is reduced to [-1/2, 1/2] revolutions in fp64 (|c| theta_d can
-// reach ~1e5 rad, where an fp32 angle would already be off by ~1e-2 rad), then
-// evaluated in fp32.
+// reach ~1e5 rad, where an fp32 angle would already be off by ~1e-2 rad); the
+// reduced angle is then evaluated by the hardware sine/cosine, which take
+// revolutions.
 __device__ __forceinline__ f32x2 rot_cs(long long c, double theta_rev) {
-  double r = (double)c * theta_rev;
-  double f = r - __builtin_rint(r);
-  float a = (float)(f * 6.283185307179586476925286766559);
-  float s, co;
-  sincosf(a, &s, &co);
-  return f32x2{co, s};
+  const double r = (double)c * theta_rev;
+  const float f = (float)(r - __builtin_rint(r));
+  return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
 }
 
 // Complex product (a.x + i a.y)(b.x + i b.y).
 __device__ __forceinline__ f32x2 cmul(f32x2 a, f32x2 b) {
   return f32x2{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x};
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_wave_base + 16 l; lds_wave_base must be the
+// same for the whole wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+// Wait until every global load of this wave, including LDS DMA, has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8 bytes read by lanes 4e + i / 4 of the group, e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Wave-wide exchange with the lane 32 positions away (the other half-wave).

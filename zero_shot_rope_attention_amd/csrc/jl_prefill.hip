@@ -29,6 +29,8 @@
 //                  each normalised on its own key set and written out with its
 //                  log-sum-exp (pass A local/base, B causal/grouped, C
 //                  local/grouped; ResearchPod transcript, prefill exchange).
+#include <type_traits>
+
 #include "jl_device.h"
 #include "jl_launch.h"
 
@@ -61,8 +63,10 @@ struct PrefillArgs {
 __device__ __forceinline__ int k_chunk(int row, int chunk) {
   return chunk ^ ((row & 7) | ((row & 16) >> 1));
 }
-// Byte offset of 16-byte chunk `c` (8 keys) in row d of the transposed V tile.
-__device__ __forceinline__ int vt_offset(int d, int c) { return d * (kBN * 2) + ((c ^ ((d >> 1) & 7)) << 4); }
+// V tiles are kept row-major (key rows of 256 bytes); 16-byte chunk c of key row
+// r is stored at chunk c ^ 4(r % 4), which makes the transposed reads of the
+// PV operand (4 keys x 64 bytes per half-wave) hit all 64 LDS banks once.
+__device__ __forceinline__ int v_chunk(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
 // Key (within a 32-key block) that MFMA row m of S^T stands for.  With this
 // permutation, lane half h holds keys 16h .. 16h+15 of the block in output
@@ -75,40 +79,291 @@ __device__ __forceinline__ float elem(const u32x4& u, int e) {
   return (e & 1) ? bf_hi(w) : bf_lo(w);
 }
 
-// S^T tile (64 keys x 32 query rows) from a K tile in LDS and the query fragment.
-__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const bf16x8 (&qf)[8], int lane, f32x16 (&s)[2]) {
+// Lane-constant LDS byte offsets of the MFMA operands within a tile.  The
+// swizzles only depend on a key row's low bits, which are the same for every
+// row a lane touches, so everything else is an immediate offset.
+struct LaneOffsets {
+  int k[8];  // K fragment of step kk (key block 0; block 1 is +32 rows)
+  int v[4];  // V^T fragment of column block nb (keys 4r + j/4 of the lane group)
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  LaneOffsets o;
   const int h = lane >> 5;
+  const int row = perm_key(lane & 31);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = 32 * kb + perm_key(lane & 31);
-    const uint8_t* rp = kbuf + row * 256;
-    f32x16 acc = {};
+  for (int kk = 0; kk < 8; ++kk) o.k[kk] = row * 256 + (k_chunk(row, 2 * kk + h) << 4);
+  const int j = lane & 15;
+  const int key = 16 * h + (j >> 2);
+  const int dcol = 16 * ((lane >> 4) & 1) + 4 * (j & 3);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(rp + (k_chunk(row, 2 * kk + h) << 4));
-      acc = mfma32(as_bf16x8(a), qf[kk], acc);
-    }
-    s[kb] = acc;
+  for (int nb = 0; nb < 4; ++nb) o.v[nb] = key * 256 + (v_chunk(key, (32 * nb + dcol) >> 3) << 4) + ((dcol & 7) << 1);
+  return o;
+}
+
+// S^T tile (64 keys x 32 query rows) from a K tile in LDS and the query
+// fragment; the two 32-key blocks accumulate side by side.
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const LaneOffsets& lo, const bf16x8 (&qf)[8],
+                                        f32x16 (&s)[2]) {
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(kbuf + lo.k[kk]);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(kbuf + lo.k[kk] + 32 * 256);
+    acc0 = mfma32(as_bf16x8(a0), qf[kk], acc0);
+    acc1 = mfma32(as_bf16x8(a1), qf[kk], acc1);
+  }
+  s[0] = acc0;
+  s[1] = acc1;
+}
+
+// Direct HBM -> LDS staging of a 64-key tile (16 KB) of V, or of K as cached:
+// 16 wave-instructions of 1 KB (4 key rows each), split over the NW waves.
+// Lane l fills physical chunk l % 16 of row 4 i + l / 16 and so fetches the
+// logical chunk that the swizzle maps there.  Rows past n_kv re-read the last
+// key (finite data whose probabilities are exactly zero).
+template <int NW, bool kIsK>
+__device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* base, int64_t kv_rs, int n_kv, int j0,
+                                         int wave, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16 / NW; ++r) {
+    const int blk = wave + r * NW;
+    const int row = 4 * blk + (lane >> 4);
+    const int pc = lane & 15;
+    const int c = kIsK ? k_chunk(row, pc) : v_chunk(row, pc);
+    const int j = min(j0 + row, n_kv - 1);
+    lds_dma16(base + (int64_t)j * kv_rs + 8 * c, lds_tile + blk * 1024);
   }
 }
 
+// Registers holding one thread's share of a K tile between its global load and
+// its LDS store (the load of tile t+2 is in flight while tile t is computed):
+// key kt, chunks c and c+8, i.e. both halves of 8 rotate-half pairs.
+template <int ITEMS>
+struct KRegs {
+  u32x4 lo[ITEMS], hi[ITEMS];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_k(KRegs<512 / NT>& r, const uint16_t* kbase, int64_t kv_rs, int n_kv, int j0,
+                                       int tid) {
+#pragma unroll
+  for (int it = 0; it < 512 / NT; ++it) {
+    const int id = tid + it * NT;
+    const int kt = id >> 3, c = id & 7;
+    const int j = min(j0 + kt, n_kv - 1);
+    const uint16_t* kp = kbase + (int64_t)j * kv_rs + 8 * c;
+    r.lo[it] = *reinterpret_cast<const u32x4*>(kp);
+    r.hi[it] = *reinterpret_cast<const u32x4*>(kp + kHalfD);
+  }
+}
+
+// Registers -> LDS: K as cached and K corrected by c(j) theta.
+template <int NT>
+__device__ __forceinline__ void store_k(const KRegs<512 / NT>& r, uint8_t* sk, uint8_t* skg, const f32x2* s_tdelta,
+                                        const f32x2* base, int j0, int g, float inv_g, int tid) {
+  const int r_mod = j0 % g;
+#pragma unroll
+  for (int it = 0; it < 512 / NT; ++it) {
+    const int id = tid + it * NT;
+    const int kt = id >> 3, c = id & 7;
+    *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c) << 4)) = r.lo[it];
+    *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c + 8) << 4)) = r.hi[it];
+    // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g
+    const int u = kt - small_div(r_mod + kt, g, inv_g);
+    const f32x2* td = s_tdelta + u * kHalfD + 8 * c;
+    const f32x2* bs = base + 8 * c;
+    u32x4 glo, ghi;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      float y1[2], y2[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int e = 2 * e2 + q2;
+        const f32x2 cs = cmul(bs[e], td[e]);
+        const float x1 = elem(r.lo[it], e), x2 = elem(r.hi[it], e);
+        y1[q2] = x1 * cs.x - x2 * cs.y;
+        y2[q2] = x2 * cs.x + x1 * cs.y;
+      }
+      glo[e2] = pack_bf16(y1[0], y1[1]);
+      ghi[e2] = pack_bf16(y2[0], y2[1]);
+    }
+    *reinterpret_cast<u32x4*>(skg + kt * 256 + (k_chunk(kt, c) << 4)) = glo;
+    *reinterpret_cast<u32x4*>(skg + kt * 256 + (k_chunk(kt, c + 8) << 4)) = ghi;
+  }
+}
+
+// Raw scores q.k of one wave's 32 query rows against one 64-key tile; masked
+// entries are -inf.  Lane (h, n) gets row n, keys j0 + 32kb + 16h + i.
+// kInterior: every key of the tile is causal for every row of the workgroup and,
+// in the bifocal mode, remote for every row -- no masks, grouped scores only.
+template <int MODE, bool kInterior, int NS>
+__device__ __forceinline__ void tile_scores(const uint8_t* sk, const uint8_t* skg, const LaneOffsets& lo,
+                                            const bf16x8 (&qf)[8], const bf16x8 (&qg)[8], int lane, int j0,
+                                            int my_p, int w, bool use_base, bool use_grp, float (&x)[NS][2][16]) {
+  const int h = lane >> 5;
+  if constexpr (kInterior) {
+    f32x16 sc[2];
+    qk_tile(MODE == kModePlain ? sk : skg, lo, MODE == kModePlain ? qf : qg, sc);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[0][kb][i] = sc[kb][i];
+  } else if constexpr (MODE == kModePlain) {
+    f32x16 sb[2];
+    qk_tile(sk, lo, qf, sb);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        x[0][kb][i] = (my_p - (j0 + 32 * kb + 16 * h + i) >= 0) ? sb[kb][i] : -INFINITY;
+  } else if constexpr (MODE == kModeBifocal) {
+    // remote keys take grouped scores, local keys base scores
+    if (use_grp) {
+      f32x16 sg[2];
+      qk_tile(skg, lo, qg, sg);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          x[0][kb][i] = (my_p - (j0 + 32 * kb + 16 * h + i) >= 0) ? sg[kb][i] : -INFINITY;
+    }
+    if (use_base) {
+      f32x16 sb[2];
+      qk_tile(sk, lo, qf, sb);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int dist = my_p - (j0 + 32 * kb + 16 * h + i);
+          const bool local = dist >= 0 && dist < w;
+          const float other = use_grp ? x[0][kb][i] : -INFINITY;
+          x[0][kb][i] = local ? sb[kb][i] : other;
+        }
+    }
+  } else {
+    f32x16 sb[2], sg[2];
+    qk_tile(sk, lo, qf, sb);
+    qk_tile(skg, lo, qg, sg);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dist = my_p - (j0 + 32 * kb + 16 * h + i);
+        const bool causal = dist >= 0;
+        const bool local = causal && dist < w;
+        x[0][kb][i] = local ? sb[kb][i] : -INFINITY;
+        x[1][kb][i] = causal ? sg[kb][i] : -INFINITY;
+        x[NS - 1][kb][i] = local ? sg[kb][i] : -INFINITY;
+      }
+  }
+}
+
+// Online softmax, first half: running maximum and (rarely) the rescale.
+// Scores stay in raw units: p = 2^(c (x - m)), c = scale * log2(e).  The
+// maximum m used in the exponent is only raised, and the accumulators
+// rescaled, when a row's maximum exceeds it by more than 8 / c (so p <= 2^8);
+// the decision is taken for the whole wave, so most tiles skip it.  Any m
+// gives the same normalised result: numerator and denominator share it.
+template <int NS>
+__device__ __forceinline__ void softmax_max(const float (&x)[NS][2][16], float (&m_run)[NS], float (&l_run)[NS],
+                                            f32x16 (&acc)[NS][4], float scale_log2) {
+  const float thr = 8.0f / scale_log2;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[s][kb][i]);
+    mloc = fmaxf(mloc, swap_halves(mloc));
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run[s] + thr)) {
+      const float m_new = fmaxf(m_run[s], mloc);
+      const float alpha = __builtin_amdgcn_exp2f((m_run[s] - m_new) * scale_log2);
+      m_run[s] = m_new;
+      l_run[s] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[s][nb] *= alpha;
+    }
+  }
+}
+
+// Online softmax, second half: probabilities (bf16 pairs) and row sums.
+template <int NS>
+__device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const float (&m_run)[NS],
+                                            float (&l_run)[NS], float scale_log2, uint32_t (&pk)[NS][2][8]) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float mc = -m_run[s] * scale_log2;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[s][kb][2 * i2], scale_log2, mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[s][kb][2 * i2 + 1], scale_log2, mc));
+        psum += p0 + p1;
+        pk[s][kb][i2] = pack_bf16(p0, p1);
+      }
+    }
+    l_run[s] += psum;
+  }
+}
+
+// O^T += V^T P^T over 4 steps of 16 keys: step (kb, half) uses keys
+// 32kb + 16h + 8half + e, which are output registers 8half + e of block kb.
+// O^T += V^T P^T over 4 steps of 16 keys: step (kb, half) uses keys
+// 32kb + 16h + 8half + e, which are output registers 8half + e of block kb.
+// The V^T operand (lane (n, h): d = 32nb + n, 8 keys) comes from two
+// transposed reads of the row-major V tile: lane j of each 16-lane group reads
+// 4 values of d at key 4r + j/4 (r = 0, 1), columns 4(j % 4) .. 4(j % 4) + 3.
+template <int NS>
+__device__ __forceinline__ void pv_tile(const uint8_t* sv, const LaneOffsets& lo, const uint32_t (&pk)[NS][2][8],
+                                        f32x16 (&acc)[NS][4]) {
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    const int kb = step >> 1, half = step & 1;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const u32x2 t0 = lds_read_tr16(sv + lo.v[nb] + (32 * kb + 8 * half) * 256);
+      const u32x2 t1 = lds_read_tr16(sv + lo.v[nb] + (32 * kb + 8 * half + 4) * 256);
+      const u32x4 vf = {t0.x, t0.y, t1.x, t1.y};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 pf = {pk[s][kb][4 * half + 0], pk[s][kb][4 * half + 1], pk[s][kb][4 * half + 2],
+                          pk[s][kb][4 * half + 3]};
+        acc[s][nb] = mfma32(as_bf16x8(vf), as_bf16x8(pf), acc[s][nb]);
+      }
+    }
+  }
+}
+
+// Software pipeline over key tiles (one barrier per tile).  Iteration t:
+//   global loads of tile t+2 -> registers          (in flight during the rest)
+//   softmax maximum / rescale on the scores of tile t (computed last iteration)
+//   scores of tile t+1 (QK MFMAs)  | probabilities of tile t (VALU)
+//   O += P V for tile t (PV MFMAs)  | registers of tile t+2 -> LDS (VALU: the
+//                                     correction rotation, V transposition)
+//   barrier
+// K tiles are double-buffered (t+1 read, t+2 written), V tiles triple-buffered
+// (t read, t+1 waiting, t+2 written).
 template <int MODE, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a) {
   constexpr int NT = NW * 64;
   constexpr bool kGrouped = MODE != kModePlain;
   constexpr int NS = (MODE == kModePasses) ? 3 : 1;
+  constexpr int kTileBytes = kBN * 256;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[kBN * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t s_kg[kGrouped ? kBN * 256 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kD * kBN * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];                  // K as cached
+  __shared__ __attribute__((aligned(16))) uint8_t s_kg[kGrouped ? 2 * kTileBytes : 16];  // corrected K
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];                  // V row-major
   __shared__ f32x2 s_tdelta[kGrouped ? 65 * kHalfD : 1];  // E(-u theta_d), u = 0..64
-  __shared__ f32x2 s_base[kGrouped ? 2 * kHalfD : 1];     // E(c(j0) theta_d), double-buffered
+  __shared__ f32x2 s_base[kGrouped ? 3 * kHalfD : 1];     // E(c(j0) theta_d) of tile u at u % 3
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;
-  const int n = lane & 31;
 
   // Workgroup -> (unit, query block).  Dispatch places consecutive workgroups
   // on consecutive XCDs; when possible every XCD keeps one KV head, so the
@@ -143,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
   const bool wave_rows = row0 < a.n_q;
   const int wp_lo = pos_off + row0;
   const int wp_hi = pos_off + min(a.n_q, row0 + 32) - 1;
-  const int my_row = row0 + n;
+  const int my_row = row0 + (lane & 31);
   const bool row_ok = my_row < a.n_q;
   const int my_p = row_ok ? pos_off + my_row : -1;  // -1: no causal key at all
 
@@ -152,15 +407,21 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
   const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
   const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
 
+  KRegs<512 / NT> kregs;
+  if constexpr (kGrouped) load_k<NT>(kregs, kbase, kv_rs, a.n_kv, 0, tid);
+
   // ---- query fragments (B operand of S^T): row my_row, d = 16kk + 8h + e ----
   bf16x8 qf[8];
   bf16x8 qg[8];
+  const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+  auto qraw_reload = [&](int kk) -> u32x4 {
+    return row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
+  };
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
     u32x4 raw[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      raw[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
+      raw[kk] = qraw_reload(kk);
       qf[kk] = as_bf16x8(raw[kk]);
     }
     if constexpr (kGrouped) {
@@ -190,11 +451,37 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
     }
   }
 
+  auto base_angles = [&](int tt, int slot) {  // E(c(j0) theta_d) of tile tt, by threads 0..63
+    const int j = tt * kBN;
+    s_base[slot * kHalfD + tid] = rot_cs((long long)(j / a.g) - j, a.theta_rev[tid]);
+  };
+  // Tile tt into LDS: V (and, plain, K) by direct copies issued here; in the
+  // bifocal modes K comes from registers loaded earlier, corrected on the way.
+  auto dma = [&](int tt, int ks, int vs) {
+    dma_tile<NW, false>(s_v + vs * kTileBytes, vbase, kv_rs, a.n_kv, tt * kBN, wave, lane);
+    if constexpr (!kGrouped) dma_tile<NW, true>(s_k + ks * kTileBytes, kbase, kv_rs, a.n_kv, tt * kBN, wave, lane);
+  };
+  auto stage_k = [&](int tt, int ks, int vs) {
+    if constexpr (kGrouped)
+      store_k<NT>(kregs, s_k + ks * kTileBytes, s_kg + ks * kTileBytes, s_tdelta, s_base + vs * kHalfD, tt * kBN,
+                  a.g, a.inv_g, tid);
+  };
+
   if constexpr (kGrouped) {
     for (int idx = tid; idx < 65 * kHalfD; idx += NT)
       s_tdelta[idx] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
-    if (tid < kHalfD) s_base[tid] = f32x2{1.0f, 0.0f};  // tile 0: c(0) = 0
+    if (tid < kHalfD)
+      for (int t = 0; t < 3; ++t) base_angles(min(t, ntiles - 1), t);
+    __syncthreads();
   }
+  dma(0, 0, 0);
+  stage_k(0, 0, 0);
+  if (ntiles > 1) {
+    dma(1, 1, 1);
+    if constexpr (kGrouped) load_k<NT>(kregs, kbase, kv_rs, a.n_kv, kBN, tid);
+    stage_k(1, 1, 1);
+  }
+  wait_vmem();
 
   float m_run[NS], l_run[NS];
   f32x16 acc[NS][4];
@@ -206,173 +493,95 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
     for (int nb = 0; nb < 4; ++nb) acc[s][nb] = f32x16{};
   }
 
+  // Interior tiles: causal for every row of the workgroup and (bifocal) remote
+  // for every row: keys j <= P0 - W with P0 the first row's position.
+  const int p0_wg = pos_off + row0_wg;
+  int n_interior = 0;
+  if constexpr (MODE == kModePlain) n_interior = min(ntiles, max(0, (p0_wg + 1) / kBN));
+  if constexpr (MODE == kModeBifocal) n_interior = min(ntiles, max(0, (p0_wg - a.w + 1) / kBN));
+
+  const LaneOffsets lofs = lane_offsets(lane);
+  auto wave_uses = [&](int t) { return wave_rows && t * kBN <= wp_hi; };
+  auto scores = [&](int t, auto interior_tag, float (&xs)[NS][2][16]) {
+    constexpr bool kInt = decltype(interior_tag)::value;
+    const int j0 = t * kBN;
+    bool use_base = true, use_grp = false;
+    if constexpr (MODE == kModeBifocal) {
+      use_grp = (j0 <= wp_hi - a.w);                 // a remote key for some row of the wave
+      use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);  // a local key for some row of the wave
+    }
+    if constexpr (MODE == kModePasses) use_grp = true;
+    tile_scores<MODE, kInt, NS>(s_k + (t & 1) * kTileBytes, s_kg + (kGrouped ? (t & 1) * kTileBytes : 0), lofs, qf,
+                                qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
+  };
+
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kBN;
+  // Scores of the current tile live in xa or xb; steps alternate the two so
+  // that no copy is needed (the loops are unrolled by two).
+  float xa[NS][2][16], xb[NS][2][16];
+  if (wave_uses(0)) {
+    if (n_interior > 0) scores(0, std::true_type{}, xa);
+    else scores(0, std::false_type{}, xa);
+  }
 
-    // ---- stage K (and corrected K) ----
-    // item: key kt, 16-byte chunks c and c+8 (the two halves of 8 rotate-half pairs)
-    bool need_grp = false;
-    int r_mod = 0;
-    if constexpr (MODE == kModeBifocal) need_grp = (j0 <= kend - 1 - a.w);  // some remote key
-    if constexpr (MODE == kModePasses) need_grp = true;
-    if constexpr (kGrouped) r_mod = j0 % a.g;
-    const f32x2* base_cur = s_base + (t & 1) * kHalfD;
-    for (int id = tid; id < kBN * 8; id += NT) {
-      const int kt = id >> 3;
-      const int c = id & 7;
-      const int j = j0 + kt;
-      u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      if (j < a.n_kv) {
-        const uint16_t* kp = kbase + (int64_t)j * kv_rs + 8 * c;
-        lo = *reinterpret_cast<const u32x4*>(kp);
-        hi = *reinterpret_cast<const u32x4*>(kp + kHalfD);
-      }
-      *reinterpret_cast<u32x4*>(s_k + kt * 256 + (k_chunk(kt, c) << 4)) = lo;
-      *reinterpret_cast<u32x4*>(s_k + kt * 256 + (k_chunk(kt, c + 8) << 4)) = hi;
-      if constexpr (kGrouped) {
-        if (need_grp) {
-          // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g
-          const int u = kt - small_div(r_mod + kt, a.g, a.inv_g);
-          const f32x2* td = s_tdelta + u * kHalfD + 8 * c;
-          const f32x2* bs = base_cur + 8 * c;
-          u32x4 glo, ghi;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            float y1[2], y2[2];
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-              const int e = 2 * e2 + q2;
-              const f32x2 cs = cmul(bs[e], td[e]);
-              const float x1 = elem(lo, e), x2 = elem(hi, e);
-              y1[q2] = x1 * cs.x - x2 * cs.y;
-              y2[q2] = x2 * cs.x + x1 * cs.y;
-            }
-            glo[e2] = pack_bf16(y1[0], y1[1]);
-            ghi[e2] = pack_bf16(y2[0], y2[1]);
-          }
-          *reinterpret_cast<u32x4*>(s_kg + kt * 256 + (k_chunk(kt, c) << 4)) = glo;
-          *reinterpret_cast<u32x4*>(s_kg + kt * 256 + (k_chunk(kt, c + 8) << 4)) = ghi;
-        }
-      }
-    }
-    // ---- stage V transposed: item = keys (2kp, 2kp+1) x d chunk dc ----
-    for (int id = tid; id < (kBN / 2) * 16; id += NT) {
-      const int kp = id >> 4;
-      const int dc = id & 15;
-      const int j = j0 + 2 * kp;
-      u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-      if (j < a.n_kv) va = *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * kv_rs + 8 * dc);
-      if (j + 1 < a.n_kv) vb = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(j + 1) * kv_rs + 8 * dc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wa = va[e >> 1], wb = vb[e >> 1];
-        const uint32_t val = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
-        const int d = 8 * dc + e;
-        *reinterpret_cast<uint32_t*>(s_vt + vt_offset(d, kp >> 2) + ((kp & 3) << 2)) = val;
-      }
-    }
-    // ---- rotation base for the next tile ----
+  auto step = [&](int t, auto next_interior_tag, float (&x_cur)[NS][2][16], float (&x_next)[NS][2][16]) {
+    constexpr bool kNextInterior = decltype(next_interior_tag)::value;
+    // Loads and staging run unconditionally (the tile index is clamped at the
+    // end: re-staging the last tile into free slots is harmless), which keeps
+    // the whole step in one basic block apart from the rare rescale.
+    const int t2 = min(t + 2, ntiles - 1);
+    dma(t2, t & 1, (t + 2) % 3);
     if constexpr (kGrouped) {
-      if (tid < kHalfD && t + 1 < ntiles) {
-        const int j1 = j0 + kBN;
-        s_base[((t + 1) & 1) * kHalfD + tid] = rot_cs((long long)(j1 / a.g) - j1, a.theta_rev[tid]);
-      }
+      load_k<NT>(kregs, kbase, kv_rs, a.n_kv, t2 * kBN, tid);
+      // rotation base of tile t+3 (its slot was last read while staging tile t)
+      if (tid < kHalfD) base_angles(min(t + 3, ntiles - 1), (t + 3) % 3);
     }
+    // interior steps: every wave with rows uses tiles t and t+1
+    const bool act = kNextInterior || wave_uses(t);
+    if (act) softmax_max<NS>(x_cur, m_run, l_run, acc, a.scale_log2);
+    // region 1: QK MFMAs of tile t+1 beside the exponentials of tile t
+    uint32_t pk[NS][2][8];
+    if (kNextInterior || (t + 1 < ntiles && wave_uses(t + 1))) scores(t + 1, next_interior_tag, x_next);
+    if (act) softmax_exp<NS>(x_cur, m_run, l_run, a.scale_log2, pk);
+    __builtin_amdgcn_sched_barrier(0);
+    // region 2: PV MFMAs of tile t beside the staging of tile t+2
+    if (act) pv_tile<NS>(s_v + (t % 3) * kTileBytes, lofs, pk, acc);
+    stage_k(t2, t & 1, (t + 2) % 3);
+    wait_vmem();
     __syncthreads();
+  };
 
-    // ---- per-wave compute ----
-    if (wave_rows && j0 <= wp_hi) {
-      bool use_base = true, use_grp = false;
-      if constexpr (MODE == kModeBifocal) {
-        use_grp = (j0 <= wp_hi - a.w);                 // a remote key for some row of the wave
-        use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);  // a local key for some row of the wave
-      }
-      if constexpr (MODE == kModePasses) {
-        use_grp = true;
-        use_base = true;
-      }
-      f32x16 sb[2], sg[2];
-      if (use_base) qk_tile(s_k, qf, lane, sb);
-      if constexpr (kGrouped) {
-        if (use_grp) qk_tile(s_kg, qg, lane, sg);
-      }
-
-      // scores in log2 units per state; keys j = j0 + 32kb + 16h + i
-      float x[NS][2][16];
+  // interior steps: t = 0 .. n_interior-2 (tile t+1 is interior)
+  int t = 0;
+  const int t_int_end = max(0, n_interior - 1);
+  for (; t + 1 < t_int_end; t += 2) {
+    step(t, std::true_type{}, xa, xb);
+    step(t + 1, std::true_type{}, xb, xa);
+  }
+  bool in_b = false;  // current scores in xb?
+  if (t < t_int_end) {
+    step(t, std::true_type{}, xa, xb);
+    ++t;
+    in_b = true;
+  }
+  if constexpr (MODE == kModeBifocal) {
+    // the base-RoPE query fragment is only needed from the band on
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int dist = my_p - (j0 + 32 * kb + 16 * h + i);
-          const bool causal = dist >= 0;
-          if constexpr (MODE == kModePlain) {
-            x[0][kb][i] = causal ? sb[kb][i] * a.scale_log2 : -INFINITY;
-          } else if constexpr (MODE == kModeBifocal) {
-            const bool local = causal && dist < a.w;
-            const float v = local ? (use_base ? sb[kb][i] : 0.0f) : (use_grp ? sg[kb][i] : 0.0f);
-            x[0][kb][i] = causal ? v * a.scale_log2 : -INFINITY;
-          } else {
-            const bool local = causal && dist < a.w;
-            x[0][kb][i] = local ? sb[kb][i] * a.scale_log2 : -INFINITY;
-            x[1][kb][i] = causal ? sg[kb][i] * a.scale_log2 : -INFINITY;
-            x[NS - 1][kb][i] = local ? sg[kb][i] * a.scale_log2 : -INFINITY;
-          }
-        }
-      }
-
-      // online softmax per state
-      uint32_t pk[NS][2][8];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[s][kb][i]);
-        mloc = fmaxf(mloc, swap_halves(mloc));
-        const float m_new = fmaxf(m_run[s], mloc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
-        m_run[s] = m_new;
-        float psum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i2 = 0; i2 < 8; ++i2) {
-            const float p0 = __builtin_amdgcn_exp2f(x[s][kb][2 * i2] - m_new);
-            const float p1 = __builtin_amdgcn_exp2f(x[s][kb][2 * i2 + 1] - m_new);
-            psum += p0 + p1;
-            pk[s][kb][i2] = pack_bf16(p0, p1);
-          }
-        }
-        l_run[s] = l_run[s] * alpha + psum;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[s][nb] *= alpha;
-      }
-
-      // O^T += V^T P^T over 4 steps of 16 keys: step (kb, half) uses keys
-      // 32kb + 16h + 8half + e, which are output registers 8half + e of block kb.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int c = 4 * kb + 2 * h + half;
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int d = 32 * nb + n;
-            const u32x4 vf = *reinterpret_cast<const u32x4*>(s_vt + vt_offset(d, c));
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const u32x4 pf = {pk[s][kb][4 * half + 0], pk[s][kb][4 * half + 1], pk[s][kb][4 * half + 2],
-                                pk[s][kb][4 * half + 3]};
-              acc[s][nb] = mfma32(as_bf16x8(vf), as_bf16x8(pf), acc[s][nb]);
-            }
-          }
-        }
-      }
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(qraw_reload(kk));
+  }
+  if (!in_b) {
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, std::false_type{}, xa, xb);
+      step(t + 1, std::false_type{}, xb, xa);
     }
-    __syncthreads();
+    if (t < ntiles) step(t, std::false_type{}, xa, xb);
+  } else {
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, std::false_type{}, xb, xa);
+      step(t + 1, std::false_type{}, xa, xb);
+    }
+    if (t < ntiles) step(t, std::false_type{}, xb, xa);
   }
 
   // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
@@ -382,7 +591,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
     const float lt = l_run[s] + swap_halves(l_run[s]);
     const bool empty = !(lt > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / lt;
-    const float lse_v = empty ? -INFINITY : (m_run[s] + __builtin_log2f(lt)) * kLn2;
+    const float lse_v = empty ? -INFINITY : (m_run[s] * a.scale_log2 + __builtin_log2f(lt)) * kLn2;
     if constexpr (MODE == kModePasses) {
       float* o = a.out_abc + ((((int64_t)s * a.batch + b) * a.n_q + my_row) * a.hq + hq) * kD;
 #pragma unroll
@@ -407,6 +616,369 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
       if (a.lse && h == 0) a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = lse_v;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong prefill (plain and bifocal).
+//
+// Waves 0-3 (group A) and 4-7 (group B) -- one of each per SIMD -- run the same
+// per-tile program half a tile apart, separated by workgroup barriers:
+//     A: | M(0) | V(0) | M(1) | V(1) | ...
+//     B: |  --  | M(0) | V(0) | M(1) | ...
+// M(k) is the MFMA phase (S = QK^T of tile k, O += P V of tile k-1) and V(k)
+// the VALU phase (softmax of tile k, staging of half a future tile), so in
+// every phase one wave of each SIMD keeps the matrix cores busy while the
+// other works on the vector ALUs.  Tile t is staged from registers loaded one
+// phase earlier: its key half 32..63 by group B in V(t-2), its half 0..31 by
+// group A in V(t-1).  K and corrected K are double-buffered, V triple-buffered.
+// ---------------------------------------------------------------------------
+
+// One group's half (32 keys) of a tile in registers: one K item (key, chunks
+// c and c+8 -- both halves of 8 rotate-half pairs) and two 16-byte V chunks.
+struct HalfTile {
+  u32x4 klo, khi, v0, v1;
+};
+
+__device__ __forceinline__ void load_half(HalfTile& r, const uint16_t* kbase, const uint16_t* vbase, int64_t kv_rs,
+                                          int n_kv, int j0, int half, int gtid) {
+  {
+    const int kt = 32 * half + (gtid >> 3), c = gtid & 7;
+    const uint16_t* kp = kbase + (int64_t)min(j0 + kt, n_kv - 1) * kv_rs + 8 * c;
+    r.klo = *reinterpret_cast<const u32x4*>(kp);
+    r.khi = *reinterpret_cast<const u32x4*>(kp + kHalfD);
+  }
+  {
+    const int row = 32 * half + (gtid >> 4), c = gtid & 15;
+    r.v0 = *reinterpret_cast<const u32x4*>(vbase + (int64_t)min(j0 + row, n_kv - 1) * kv_rs + 8 * c);
+    r.v1 = *reinterpret_cast<const u32x4*>(vbase + (int64_t)min(j0 + row + 16, n_kv - 1) * kv_rs + 8 * c);
+  }
+}
+
+template <bool kGrouped>
+__device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8_t* skg, uint8_t* sv,
+                                           const f32x2* s_tdelta, const f32x2* base, int j0, int g, float inv_g,
+                                           int half, int gtid) {
+  {
+    const int row = 32 * half + (gtid >> 4), c = gtid & 15;
+    *reinterpret_cast<u32x4*>(sv + row * 256 + (v_chunk(row, c) << 4)) = r.v0;
+    *reinterpret_cast<u32x4*>(sv + (row + 16) * 256 + (v_chunk(row + 16, c) << 4)) = r.v1;
+  }
+  const int kt = 32 * half + (gtid >> 3), c = gtid & 7;
+  *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c) << 4)) = r.klo;
+  *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c + 8) << 4)) = r.khi;
+  if constexpr (kGrouped) {
+    // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g; the
+    // 8 pairs are rotated two at a time to keep few values live.
+    const int u = kt - small_div(j0 % g + kt, g, inv_g);
+    const f32x2* td = s_tdelta + u * kHalfD + 8 * c;
+    const f32x2* bs = base + 8 * c;
+    u32x4 glo, ghi;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      float y1[2], y2[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int e = 2 * e2 + q2;
+        const f32x2 cs = cmul(bs[e], td[e]);
+        const float x1 = elem(r.klo, e), x2 = elem(r.khi, e);
+        y1[q2] = x1 * cs.x - x2 * cs.y;
+        y2[q2] = x2 * cs.x + x1 * cs.y;
+      }
+      glo[e2] = pack_bf16(y1[0], y1[1]);
+      ghi[e2] = pack_bf16(y2[0], y2[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    *reinterpret_cast<u32x4*>(skg + kt * 256 + (k_chunk(kt, c) << 4)) = glo;
+    *reinterpret_cast<u32x4*>(skg + kt * 256 + (k_chunk(kt, c + 8) << 4)) = ghi;
+  }
+}
+
+
+// Interior MFMA phase: S = K Q^T of tile k (16 MFMAs, two 32-key blocks) and,
+// when kPV, O^T += V^T P^T of tile k-1 (16 MFMAs), issued alternately.  The
+// LDS operands of step i+3 are read while the MFMAs of step i run (a ring of 4
+// operand sets), and the order is pinned so the compiler does not hoist all 48
+// reads ahead of the matrix work.
+template <bool kPV>
+__device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8_t* vbuf, const LaneOffsets& lo,
+                                                const bf16x8 (&q)[8], const uint32_t (&pk)[1][2][8],
+                                                f32x16 (&sc)[2], f32x16 (&acc)[1][4]) {
+  constexpr int kDist = 2;
+  auto read_k = [&](int i) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(kbuf + lo.k[i >> 1] + (i & 1) * (32 * 256));
+  };
+  auto read_v = [&](int i) -> u32x4 {
+    const int st = i >> 2, nb = i & 3;
+    const int kb = st >> 1, half = st & 1;
+    const u32x2 t0 = lds_read_tr16(vbuf + lo.v[nb] + (32 * kb + 8 * half) * 256);
+    const u32x2 t1 = lds_read_tr16(vbuf + lo.v[nb] + (32 * kb + 8 * half + 4) * 256);
+    return u32x4{t0.x, t0.y, t1.x, t1.y};
+  };
+  u32x4 kr[kDist + 1], vr[kDist + 1];
+#pragma unroll
+  for (int i = 0; i < kDist; ++i) {
+    kr[i] = read_k(i);
+    if constexpr (kPV) vr[i] = read_v(i);
+  }
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + kDist < 16) {
+      kr[(i + kDist) % (kDist + 1)] = read_k(i + kDist);
+      if constexpr (kPV) vr[(i + kDist) % (kDist + 1)] = read_v(i + kDist);
+    }
+    const bf16x8 ka = as_bf16x8(kr[i % (kDist + 1)]);
+    if (i & 1) s1 = mfma32(ka, q[i >> 1], s1);
+    else s0 = mfma32(ka, q[i >> 1], s0);
+    if constexpr (kPV) {
+      const int st = i >> 2, nb = i & 3;
+      const int kb = st >> 1, half = st & 1;
+      const u32x4 pf = {pk[0][kb][4 * half], pk[0][kb][4 * half + 1], pk[0][kb][4 * half + 2],
+                        pk[0][kb][4 * half + 3]};
+      acc[0][nb] = mfma32(as_bf16x8(vr[i % (kDist + 1)]), as_bf16x8(pf), acc[0][nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sc[0] = s0;
+  sc[1] = s1;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
+  static_assert(MODE == kModePlain || MODE == kModeBifocal, "ping-pong kernel: plain or bifocal");
+  constexpr bool kGrouped = MODE == kModeBifocal;
+  constexpr int kTileBytes = kBN * 256;
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];                  // K as cached
+  __shared__ __attribute__((aligned(16))) uint8_t s_kg[kGrouped ? 2 * kTileBytes : 16];  // corrected K
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];                  // V row-major
+  __shared__ f32x2 s_tdelta[kGrouped ? 64 * kHalfD : 1];  // E(-u theta_d), u = 0..63
+  __shared__ f32x2 s_base[kGrouped ? 4 * kHalfD : 1];     // E(c(j0) theta_d): [group][parity of k]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int gtid = tid & 255;
+  const int h = lane >> 5;
+
+  int unit, rank;
+  {
+    const int id = blockIdx.x;
+    if ((a.n_units & 7) == 0) {
+      const int slot = id >> 3;
+      unit = (id & 7) + 8 * (slot / a.n_qblocks);
+      rank = slot % a.n_qblocks;
+    } else {
+      unit = id / a.n_qblocks;
+      rank = id % a.n_qblocks;
+    }
+  }
+  const int qb = a.n_qblocks - 1 - rank;
+  const int n_hg = a.grp / a.hpw;
+  const int hg = unit % n_hg;
+  const int bk = unit / n_hg;
+  const int kvh = bk % a.hkv;
+  const int b = bk / a.hkv;
+  const int hq = kvh * a.grp + hg * a.hpw + (wave % a.hpw);
+  const int row0_wg = qb * a.bm;
+  const int row0 = row0_wg + (wave / a.hpw) * 32;
+  const int pos_off = a.n_kv - a.n_q;
+  const int last_row_wg = min(a.n_q, row0_wg + a.bm) - 1;
+  const int kend = pos_off + last_row_wg + 1;
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  const bool wave_rows = row0 < a.n_q;
+  const int wp_lo = pos_off + row0;
+  const int wp_hi = pos_off + min(a.n_q, row0 + 32) - 1;
+  const int my_row = row0 + (lane & 31);
+  const bool row_ok = my_row < a.n_q;
+  const int my_p = row_ok ? pos_off + my_row : -1;
+
+  const int64_t q_rs = (int64_t)a.hq * kD;
+  const int64_t kv_rs = (int64_t)a.hkv * kD;
+  const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+  const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+
+  // rotation table first, while few values are live
+  if constexpr (kGrouped) {
+#pragma unroll 1
+    for (int idx = tid; idx < 64 * kHalfD; idx += 512)
+      s_tdelta[idx] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
+  }
+  HalfTile regs;
+  load_half(regs, kbase, vbase, kv_rs, a.n_kv, 0, grp, gtid);
+
+  bf16x8 qf[8];
+  bf16x8 qg[8];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+    u32x4 raw[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      raw[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
+      qf[kk] = as_bf16x8(raw[kk]);
+    }
+    if constexpr (kGrouped) {
+      const long long cq = row_ok ? (long long)(my_p / a.g) - my_p : 0;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 lo, hi;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int e = 2 * e2 + t;
+            const f32x2 cs = rot_cs(cq, a.theta_rev[16 * kk + 8 * h + e]);
+            const float x1 = elem(raw[kk], e), x2 = elem(raw[kk + 4], e);
+            y1[t] = x1 * cs.x - x2 * cs.y;
+            y2[t] = x2 * cs.x + x1 * cs.y;
+          }
+          lo[e2] = pack_bf16(y1[0], y1[1]);
+          hi[e2] = pack_bf16(y2[0], y2[1]);
+        }
+        qg[kk] = as_bf16x8(lo);
+        qg[kk + 4] = as_bf16x8(hi);
+      }
+    }
+  }
+
+  auto base_angles = [&](int tt, int slot) {  // by the first 64 threads of a group
+    const int j = min(tt, ntiles - 1) * kBN;
+    s_base[slot * kHalfD + (gtid & 63)] = rot_cs((long long)(j / a.g) - j, a.theta_rev[gtid & 63]);
+  };
+  auto store = [&](int tt, int slot) {  // slot: rotation-base slot
+    store_half<kGrouped>(regs, s_k + (tt & 1) * kTileBytes, s_kg + (kGrouped ? (tt & 1) * kTileBytes : 0),
+                         s_v + (tt % 3) * kTileBytes, s_tdelta, s_base + (kGrouped ? slot * kHalfD : 0), tt * kBN,
+                         a.g, a.inv_g, grp, gtid);
+  };
+
+  // ---- prologue: tiles 0 and 1, each group its half ----
+  // s_base slot [grp][k & 1] holds the rotation base of the tile group grp
+  // stages in V(k); the prologue borrows slot [grp][0] for tiles 0 and 1.
+  if constexpr (kGrouped) {
+    if (gtid < 64) {
+      s_base[(2 * grp) * kHalfD + gtid] = rot_cs(0, a.theta_rev[gtid]);  // tile 0: c(0) = 0
+    }
+    __syncthreads();
+  }
+  store(0, 2 * grp);
+  __syncthreads();
+  if (ntiles > 1) {
+    if constexpr (kGrouped) {
+      if (gtid < 64) base_angles(1, 2 * grp);
+      __syncthreads();
+    }
+    load_half(regs, kbase, vbase, kv_rs, a.n_kv, kBN, grp, gtid);
+    store(1, 2 * grp);
+  }
+  if constexpr (kGrouped) {
+    __syncthreads();
+    // slot [grp][k & 1] holds the base of the tile staged in V(k): the first
+    // in-loop stagings are V(1) (group A, tile 2) and V(0) (group B, tile 2)
+    if (gtid < 64) {
+      base_angles(2, 2 * grp + (grp == 0 ? 1 : 0));
+    }
+  }
+
+  const LaneOffsets lofs = lane_offsets(lane);
+  float m_run[1] = {kNegBig}, l_run[1] = {0.0f};
+  f32x16 acc[1][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[0][nb] = f32x16{};
+
+  const int p0_wg = pos_off + row0_wg;
+  int n_interior = 0;
+  if constexpr (MODE == kModePlain) n_interior = min(ntiles, max(0, (p0_wg + 1) / kBN));
+  if constexpr (MODE == kModeBifocal) n_interior = min(ntiles, max(0, (p0_wg - a.w + 1) / kBN));
+  auto uses = [&](int t) { return wave_rows && t * kBN <= wp_hi; };
+
+  float xs[1][2][16];
+  uint32_t pk[1][2][8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk[0][kb][i] = 0u;
+  const int ahead = grp == 0 ? 1 : 2;  // A stages tile k+1, B tile k+2
+
+  __syncthreads();
+  if (grp == 1) __syncthreads();  // group B runs one phase behind
+
+  // One tile of the ping-pong program: phase M(k), barrier, phase V(k), barrier.
+  auto tile = [&](int k, auto interior_tag) {
+    constexpr bool kInt = decltype(interior_tag)::value;
+    const int tt = k + ahead;
+    const bool do_stage = tt < ntiles && tt >= 2;
+    if (do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, grp, gtid);
+    const uint8_t* sk = s_k + (k & 1) * kTileBytes;
+    const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
+    // V of tile k-1 (at k = 0 the probabilities are zero and tile 0's finite V
+    // is read instead, which adds exactly nothing)
+    const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) % 3) * kTileBytes;
+    if constexpr (kInt) {
+      f32x16 sc[2];
+      mphase_interior<true>(kGrouped ? skg : sk, svp, lofs, kGrouped ? qg : qf, pk, sc, acc);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[0][kb][i] = sc[kb][i];
+    } else {
+      const int j0 = k * kBN;
+      if (uses(k)) {
+        bool use_base = true, use_grp = false;
+        if constexpr (MODE == kModeBifocal) {
+          use_grp = (j0 <= wp_hi - a.w);
+          use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);
+        }
+        tile_scores<MODE, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
+      }
+      if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
+    }
+    __syncthreads();
+    // ---- V(k): softmax of tile k, staging ----
+    if (kInt || uses(k)) {
+      softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
+      softmax_exp<1>(xs, m_run, l_run, a.scale_log2, pk);
+    }
+    // the scores are dead once the probabilities exist: keep the staging after
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_stage) store(tt, 2 * grp + (k & 1));
+    if constexpr (kGrouped) {
+      // base of the tile this group stages in V(k+1), into the other slot
+      if (gtid < 64) base_angles(tt + 1, 2 * grp + ((k + 1) & 1));
+    }
+    __syncthreads();
+  };
+
+  int k = 0;
+  for (; k < n_interior; ++k) tile(k, std::true_type{});
+  if constexpr (MODE == kModeBifocal) {
+    // the base-RoPE query fragment is only needed from the band on
+    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+  }
+  for (; k < ntiles; ++k) tile(k, std::false_type{});
+  if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lofs, pk, acc);
+  if (grp == 0) __syncthreads();
+
+  // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
+  if (!row_ok) return;
+  const float lt = l_run[0] + swap_halves(l_run[0]);
+  const float inv = 1.0f / lt;
+  const float lse_v = (m_run[0] * a.scale_log2 + __builtin_log2f(lt)) * kLn2;
+  uint16_t* o = a.out + (((int64_t)b * a.n_q + my_row) * a.hq + hq) * kD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      u32x2 val = {pack_bf16(acc[0][nb][4 * i4] * inv, acc[0][nb][4 * i4 + 1] * inv),
+                   pack_bf16(acc[0][nb][4 * i4 + 2] * inv, acc[0][nb][4 * i4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(o + 32 * nb + 8 * i4 + 4 * h) = val;
+    }
+  if (a.lse && h == 0) a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = lse_v;
 }
 
 template <int MODE, int NW>
@@ -444,7 +1016,10 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   const long long blocks = (long long)a.n_units * a.n_qblocks;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<MODE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+  if constexpr (MODE == kModePasses)
+    hipLaunchKernelGGL((prefill_kernel<MODE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_pp_kernel<MODE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
