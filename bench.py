@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the plain-prefill and decode comparisons")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run one 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -93,6 +95,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB (1073741824 bytes read, 1073741824 bytes written)")
+        return
 
     import zero_shot_rope_attention_amd as jl
     from zero_shot_rope_attention_amd.inputs import make_qkv

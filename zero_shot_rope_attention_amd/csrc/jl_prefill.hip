@@ -68,6 +68,11 @@ __device__ __forceinline__ int k_chunk(int row, int chunk) {
 // PV operand (4 keys x 64 bytes per half-wave) hit all 64 LDS banks once.
 __device__ __forceinline__ int v_chunk(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
+// Rows of the small-angle rotation table E(-u theta_d) are padded by 16 bytes,
+// so that threads staging different keys (different u) with the same d
+// columns fall on different LDS banks.
+constexpr int kTdStride = kHalfD + 2;
+
 // Key (within a 32-key block) that MFMA row m of S^T stands for.  With this
 // permutation, lane half h holds keys 16h .. 16h+15 of the block in output
 // registers 0..15, so a lane's probabilities form B operands of O^T = V^T P^T
@@ -670,7 +675,7 @@ __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8
     // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g; the
     // 8 pairs are rotated two at a time to keep few values live.
     const int u = kt - small_div(j0 % g + kt, g, inv_g);
-    const f32x2* td = s_tdelta + u * kHalfD + 8 * c;
+    const f32x2* td = s_tdelta + u * kTdStride + 8 * c;
     const f32x2* bs = base + 8 * c;
     u32x4 glo, ghi;
 #pragma unroll
@@ -752,7 +757,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];                  // K as cached
   __shared__ __attribute__((aligned(16))) uint8_t s_kg[kGrouped ? 2 * kTileBytes : 16];  // corrected K
   __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];                  // V row-major
-  __shared__ f32x2 s_tdelta[kGrouped ? 64 * kHalfD : 1];  // E(-u theta_d), u = 0..63
+  __shared__ f32x2 s_tdelta[kGrouped ? 64 * kTdStride : 1];  // E(-u theta_d), u = 0..63, padded rows
   __shared__ f32x2 s_base[kGrouped ? 4 * kHalfD : 1];     // E(c(j0) theta_d): [group][parity of k]
 
   const int tid = threadIdx.x;
@@ -804,7 +809,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   if constexpr (kGrouped) {
 #pragma unroll 1
     for (int idx = tid; idx < 64 * kHalfD; idx += 512)
-      s_tdelta[idx] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
+      s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
   }
   HalfTile regs;
   load_half(regs, kbase, vbase, kv_rs, a.n_kv, 0, grp, gtid);
@@ -906,8 +911,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   if (grp == 1) __syncthreads();  // group B runs one phase behind
 
   // One tile of the ping-pong program: phase M(k), barrier, phase V(k), barrier.
-  auto tile = [&](int k, auto interior_tag) {
-    constexpr bool kInt = decltype(interior_tag)::value;
+  // Tile kinds: kInterior (all keys causal and, bifocal, remote for every row
+  // of the workgroup: grouped scores, no masks), kEdge (bifocal: keys local for
+  // some rows and remote for others: both score kinds) and kLocal (every causal
+  // key local for every row: base scores with the causal mask).  Only the one
+  // or two edge tiles of a sweep keep both query fragments live.
+  constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
+  auto tile = [&](int k, auto kind_tag) {
+    constexpr int kKind = decltype(kind_tag)::value;
     const int tt = k + ahead;
     const bool do_stage = tt < ntiles && tt >= 2;
     if (do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, grp, gtid);
@@ -916,7 +927,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // V of tile k-1 (at k = 0 the probabilities are zero and tile 0's finite V
     // is read instead, which adds exactly nothing)
     const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) % 3) * kTileBytes;
-    if constexpr (kInt) {
+    if constexpr (kKind == kInterior) {
       f32x16 sc[2];
       mphase_interior<true>(kGrouped ? skg : sk, svp, lofs, kGrouped ? qg : qf, pk, sc, acc);
 #pragma unroll
@@ -926,41 +937,56 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     } else {
       const int j0 = k * kBN;
       if (uses(k)) {
-        bool use_base = true, use_grp = false;
-        if constexpr (MODE == kModeBifocal) {
-          use_grp = (j0 <= wp_hi - a.w);
-          use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);
+        if constexpr (kKind == kEdge) {
+          const bool use_grp = (j0 <= wp_hi - a.w);
+          const bool use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);
+          tile_scores<MODE, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
+        } else {
+          tile_scores<kModePlain, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, true, false, xs);
         }
-        tile_scores<MODE, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
       }
       if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
     }
     __syncthreads();
     // ---- V(k): softmax of tile k, staging ----
-    if (kInt || uses(k)) {
+    if (kKind == kInterior || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
       softmax_exp<1>(xs, m_run, l_run, a.scale_log2, pk);
     }
     // the scores are dead once the probabilities exist: keep the staging after
     __builtin_amdgcn_sched_barrier(0);
-    if (do_stage) store(tt, 2 * grp + (k & 1));
-    if constexpr (kGrouped) {
+    if (do_stage) {
+      if constexpr (kKind == kLocal)  // every later tile is local: no corrected keys needed
+        store_half<false>(regs, s_k + (tt & 1) * kTileBytes, nullptr, s_v + (tt % 3) * kTileBytes, nullptr,
+                          nullptr, 0, 1, 1.0f, grp, gtid);
+      else
+        store(tt, 2 * grp + (k & 1));
+    }
+    if constexpr (kGrouped && kKind != kLocal) {
       // base of the tile this group stages in V(k+1), into the other slot
       if (gtid < 64) base_angles(tt + 1, 2 * grp + ((k + 1) & 1));
     }
     __syncthreads();
   };
 
+  // first tile whose causal keys are local for every row of the workgroup
+  int t_local = n_interior;
+  if constexpr (MODE == kModeBifocal) {
+    const int first_all_local = pos_off + last_row_wg - a.w + 1;
+    t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
+    t_local = min(ntiles, max(n_interior, t_local));
+  }
   int k = 0;
-  for (; k < n_interior; ++k) tile(k, std::true_type{});
+  for (; k < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{});
   if constexpr (MODE == kModeBifocal) {
     // the base-RoPE query fragment is only needed from the band on
     const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+    for (; k < t_local; ++k) tile(k, std::integral_constant<int, kEdge>{});
   }
-  for (; k < ntiles; ++k) tile(k, std::false_type{});
+  for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{});
   if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lofs, pk, acc);
   if (grp == 0) __syncthreads();
 
