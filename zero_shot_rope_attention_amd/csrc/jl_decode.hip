@@ -56,18 +56,35 @@ __device__ __forceinline__ float elem(const u32x4& u, int e) {
   return (e & 1) ? bf_hi(w) : bf_lo(w);
 }
 
-// transposed V tile of one wave: [128 d][32 keys] bf16, 64-byte rows, swizzled
-__device__ __forceinline__ int vt_off(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
+
+// V tiles in LDS: row-major, 256-byte key rows, chunk c of row r stored at c ^ 4(r % 4)
+__device__ __forceinline__ int v_chunk(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+constexpr int kBlk = 32;              // keys per MFMA block
+constexpr int kVmemPerBlock = 16;     // 8 K loads + 8 V copies per block and lane
+constexpr int kVBlockBytes = kBlk * 256;
 
 template <bool BIF>
 __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kWaves][kD * 32 * 2];
+  // per-wave V blocks, double-buffered; two separate objects so that the
+  // compiler can tell which direct copy a transposed read waits for
+  __shared__ __attribute__((aligned(16))) uint8_t s_v0[kWaves][kVBlockBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v1[kWaves][kVBlockBytes];
+  __shared__ float s_fb[kWaves][kHalfD];  // per wave: c(ws) theta_d / (2 pi), reduced to [-1/2, 1/2]
+  __shared__ float s_th[kWaves][kHalfD];  // theta_d / (2 pi)
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][kMaxGroup];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int n = lane & 31;
   const int sp = blockIdx.x;
@@ -90,6 +107,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   const int64_t kv_rs = (int64_t)a.hkv * kD;
   const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
   const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+
+  // ---- per-block loads: K fragment into registers (key j0 + perm_key(n),
+  // d = 16kk + 8h + e), V rows into this wave's LDS buffer by direct copies ----
+  auto issue = [&](int blk, u32x4 (&kr)[8], int buf) {
+    const int j0 = ws + blk * kBlk;
+    const uint16_t* kp = kbase + (int64_t)min(j0 + perm_key(n), we - 1) * kv_rs + 8 * h;  // we >= 1
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kr[kk] = *reinterpret_cast<const u32x4*>(kp + 16 * kk);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = 4 * r + (lane >> 4);
+      const int c = v_chunk(row, lane & 15);
+      lds_dma16(vbase + (int64_t)min(j0 + row, we - 1) * kv_rs + 8 * c,
+                buf ? &s_v1[wave][r * 1024] : &s_v0[wave][r * 1024]);
+    }
+  };
+  u32x4 ka[8], kb[8];
 
   // query fragment (B operand of S^T): column n = query head kvh*G + n (n < G)
   bf16x8 qf[8];
@@ -131,58 +165,51 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   // Remote keys: c(j) = c(ws) - u(j), u = t - floor((r + t)/g), t = j - ws,
   // r = ws mod g.  The angle c(ws) theta_d is reduced in fp64 once per wave;
   // the small per-key part u theta_d (u < 128) is exact enough in fp32.
-  float fb[4][8], th[4][8];
   int r_s = 0;
   if (BIF && remote) {
     const long long cb = (long long)(ws / a.g) - ws;
     r_s = ws % a.g;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 16 * kk + 8 * h + e;
-        const double r = (double)cb * a.theta_rev[d];
-        fb[kk][e] = (float)(r - __builtin_rint(r));
-        th[kk][e] = a.theta_rev32[d];
-      }
+    const double r = (double)cb * a.theta_rev[lane];
+    s_fb[wave][lane] = (float)(r - __builtin_rint(r));
+    s_th[wave][lane] = a.theta_rev32[lane];
+    __builtin_amdgcn_wave_barrier();
   }
 
+  // first two blocks in flight (after the query and table loads above, whose
+  // completion the loop then never has to wait for)
+  issue(0, ka, 0);
+  issue(1, kb, 1);
+
+  // lane-constant part of the transposed V reads (see the prefill kernel)
+  const int jl = lane & 15;
+  const int vkey = 16 * h + (jl >> 2);
+  const int dcol = 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
+  int voff[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) voff[nb] = vkey * 256 + (v_chunk(vkey, (32 * nb + dcol) >> 3) << 4) + ((dcol & 7) << 1);
+
   float m_run = kNegBig, l_run = 0.0f;
+  const float thr = 8.0f / a.scale_log2;
   f32x16 acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x16{};
-  uint8_t* vt = s_vt[wave];
 
-  for (int j0 = ws; j0 < we; j0 += 32) {
-    // ---- key fragment for key j0 + perm_key(n), d = 16kk + 8h + e ----
-    const int jk = j0 + perm_key(n);
-    const bool k_ok = jk < we;
-    u32x4 kr[8];
-    {
-      const uint16_t* kp = kbase + (int64_t)(k_ok ? jk : ws) * kv_rs + 8 * h;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        kr[kk] = k_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * kk) : u32x4{0, 0, 0, 0};
-    }
-    // ---- V rows for the transposed LDS tile: items (4 keys, 8-d chunk) ----
-    u32x4 vr[2][4];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = lane + 64 * it;
-      const int kg = item >> 4, dc = item & 15;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int j = j0 + 4 * kg + q4;
-        vr[it][q4] = (j < we) ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * kv_rs + 8 * dc)
-                              : u32x4{0, 0, 0, 0};
-      }
-    }
+  auto process = [&](int blk, u32x4 (&kr)[8], int buf, bool more) {
+    const int j0 = ws + blk * kBlk;
+    // block blk's loads are older than the (up to) 16 of block blk+1
+    if (more) wait_vmem_at_most<kVmemPerBlock>();
+    else wait_vmem_at_most<0>();
     if (BIF && remote) {
-      const int t = jk - ws;
-      const int u = t - small_div(r_s + t, a.g, a.inv_g);
-      const float uf = (float)u;
+      const int t = j0 + perm_key(n) - ws;
+      const float uf = (float)(t - small_div(r_s + t, a.g, a.inv_g));
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        const float4 fb0 = *reinterpret_cast<const float4*>(&s_fb[wave][16 * kk + 8 * h]);
+        const float4 fb1 = *reinterpret_cast<const float4*>(&s_fb[wave][16 * kk + 8 * h + 4]);
+        const float4 th0 = *reinterpret_cast<const float4*>(&s_th[wave][16 * kk + 8 * h]);
+        const float4 th1 = *reinterpret_cast<const float4*>(&s_th[wave][16 * kk + 8 * h + 4]);
+        const float fbv[8] = {fb0.x, fb0.y, fb0.z, fb0.w, fb1.x, fb1.y, fb1.z, fb1.w};
+        const float thv[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
         u32x4 lo, hi;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -190,7 +217,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             const int e = 2 * e2 + q2;
-            const float rev = fb[kk][e] - uf * th[kk][e];  // angle in revolutions
+            const float rev = fbv[e] - uf * thv[e];  // angle in revolutions
             const float co = __builtin_amdgcn_cosf(rev);
             const float si = __builtin_amdgcn_sinf(rev);
             const float x1 = elem(kr[kk], e), x2 = elem(kr[kk + 4], e);
@@ -208,65 +235,69 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = mfma32(as_bf16x8(kr[kk]), qf[kk], s);
 
-    // ---- online softmax: lane holds head n, keys j0 + 16h + i ----
-    float x[16];
+    // online softmax (lazy rescale, as in the prefill): lane = head n, keys j0 + 16h + i
     float mloc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      x[i] = (j0 + 16 * h + i < we) ? s[i] * a.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, x[i]);
+      if (j0 + 16 * h + i >= we) s[i] = -INFINITY;
+      mloc = fmaxf(mloc, s[i]);
     }
     mloc = fmaxf(mloc, swap_halves(mloc));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + thr)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
+    }
+    const float mc = -m_run * a.scale_log2;
     uint32_t pk[8];
     float psum = 0.0f;
 #pragma unroll
     for (int i2 = 0; i2 < 8; ++i2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[2 * i2] - m_new);
-      const float p1 = __builtin_amdgcn_exp2f(x[2 * i2 + 1] - m_new);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i2], a.scale_log2, mc));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i2 + 1], a.scale_log2, mc));
       psum += p0 + p1;
       pk[i2] = pack_bf16(p0, p1);
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
-
-    // ---- V^T tile: for each d, 4 consecutive keys -> one 8-byte LDS store ----
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = lane + 64 * it;
-      const int kg = item >> 4, dc = item & 15;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t v0 = (vr[it][0][e >> 1] >> sh) & 0xffffu, v1 = (vr[it][1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t v2 = (vr[it][2][e >> 1] >> sh) & 0xffffu, v3 = (vr[it][3][e >> 1] >> sh) & 0xffffu;
-        const int d = 8 * dc + e;
-        *reinterpret_cast<u32x2*>(vt + vt_off(d, kg >> 1) + ((kg & 1) << 3)) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+    l_run += psum;
+    // O^T += V^T P^T: keys 16h + 8half + e
+    const uint8_t* sv = buf ? &s_v1[wave][0] : &s_v0[wave][0];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const u32x4 pf = {pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]};
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + vt_off(32 * nb + n, 2 * h + half));
+        const u32x2 t0 = lds_read_tr16(sv + voff[nb] + (8 * half) * 256);
+        const u32x2 t1 = lds_read_tr16(sv + voff[nb] + (8 * half + 4) * 256);
+        const u32x4 vf = {t0.x, t0.y, t1.x, t1.y};
         acc[nb] = mfma32(as_bf16x8(vf), as_bf16x8(pf), acc[nb]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
-  }
+  };
+
+  // Fully unrolled over the 4 blocks of a wave, with every load issued
+  // unconditionally (blocks past the end of the wave's range re-read its last
+  // key and are masked out entirely), so that the waits on the prefetched
+  // block are exact.
+  static_assert(kKeysPerWave == 4 * kBlk, "four blocks per wave");
+  process(0, ka, 0, true);
+  __builtin_amdgcn_wave_barrier();  // the V buffer is free again once its reads returned
+  issue(2, ka, 0);
+  process(1, kb, 1, true);
+  __builtin_amdgcn_wave_barrier();
+  issue(3, kb, 1);
+  process(2, ka, 0, true);
+  process(3, kb, 1, false);
 
   // ---- merge the four waves' partial softmaxes of this chunk ----
   const float lt = l_run + swap_halves(l_run);
-  __syncthreads();  // every wave is done with its V^T tile
-  float* red = reinterpret_cast<float*>(&s_vt[0][0]);  // [wave][G][D] fp32
+  __syncthreads();  // every wave is done with its V buffers
+  float* red = reinterpret_cast<float*>(&s_v0[0][0]);  // [wave][G][D] fp32 (32 KB)
   if (n < a.grp) {
     if (h == 0) {
-      s_m[wave][n] = m_run;
+      s_m[wave][n] = m_run * a.scale_log2;  // log2 units
       s_l[wave][n] = lt;
     }
     float* dst = red + ((size_t)wave * a.grp + n) * kD;
@@ -280,12 +311,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   __syncthreads();
   for (int item = tid; item < a.grp * kD; item += kWaves * 64) {
     const int hh = item / kD, d = item % kD;
-    float mx = kNegBig;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][hh]);
+    for (int w = 0; w < kWaves; ++w)
+      if (s_l[w][hh] > 0.0f) mx = fmaxf(mx, s_m[w][hh]);
     float lsum = 0.0f, o = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
+      if (!(s_l[w][hh] > 0.0f)) continue;
       const float sc = __builtin_amdgcn_exp2f(s_m[w][hh] - mx);
       lsum += s_l[w][hh] * sc;
       o += red[((size_t)w * a.grp + hh) * kD + d] * sc;
@@ -320,6 +353,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
   const int grp = tid >> 5, c4 = tid & 31;
   float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   float wsum = 0.0f;
+#pragma unroll 4
   for (int s = grp; s < n_wg; s += 8) {
     const float w = __expf(pl[s] - mx);
     const float4 x = *reinterpret_cast<const float4*>(part_o + (bh * n_wg + s) * kD + 4 * c4);

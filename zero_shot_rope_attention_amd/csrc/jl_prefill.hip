@@ -640,6 +640,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
 
 // One group's half (32 keys) of a tile in registers: one K item (key, chunks
 // c and c+8 -- both halves of 8 rotate-half pairs) and two 16-byte V chunks.
+// K items: runs of 8 lanes read the 8 chunk pairs of one key (coalesced rows).
+__device__ __forceinline__ int half_tile_key(int gtid) { return gtid >> 3; }
+__device__ __forceinline__ int half_tile_chunk(int gtid) { return gtid & 7; }
 struct HalfTile {
   u32x4 klo, khi, v0, v1;
 };
@@ -647,7 +650,7 @@ struct HalfTile {
 __device__ __forceinline__ void load_half(HalfTile& r, const uint16_t* kbase, const uint16_t* vbase, int64_t kv_rs,
                                           int n_kv, int j0, int half, int gtid) {
   {
-    const int kt = 32 * half + (gtid >> 3), c = gtid & 7;
+    const int kt = 32 * half + half_tile_key(gtid), c = half_tile_chunk(gtid);
     const uint16_t* kp = kbase + (int64_t)min(j0 + kt, n_kv - 1) * kv_rs + 8 * c;
     r.klo = *reinterpret_cast<const u32x4*>(kp);
     r.khi = *reinterpret_cast<const u32x4*>(kp + kHalfD);
@@ -668,7 +671,7 @@ __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8
     *reinterpret_cast<u32x4*>(sv + row * 256 + (v_chunk(row, c) << 4)) = r.v0;
     *reinterpret_cast<u32x4*>(sv + (row + 16) * 256 + (v_chunk(row + 16, c) << 4)) = r.v1;
   }
-  const int kt = 32 * half + (gtid >> 3), c = gtid & 7;
+  const int kt = 32 * half + half_tile_key(gtid), c = half_tile_chunk(gtid);
   *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c) << 4)) = r.klo;
   *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c + 8) << 4)) = r.khi;
   if constexpr (kGrouped) {
