@@ -173,7 +173,7 @@ def main():
                    "group_factor": g},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel<bifocal>", "flops_per_launch": flops,
+                     "kernel": "prefill_pp_kernel<1> (bifocal)", "flops_per_launch": flops,
                      "avg_launch_ms": round(pre_avg, 4)},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
         "decode_in_step_us": round(float(np.mean(dec_ms)) * 1e3, 2),
