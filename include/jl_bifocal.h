@@ -66,7 +66,7 @@ typedef int32_t jl_status;
 #define JL_OK              0
 #define JL_ERR_INVALID_ARG 1 /* null/misaligned pointer, size < 1, n_q > n_kv, Hq % Hkv != 0,
                                 L < 1, W < 1, W > L, rope_base <= 1 or not finite            */
-#define JL_ERR_UNSUPPORTED 2 /* head_dim != 128, or sizes whose element offsets overflow int64 */
+#define JL_ERR_UNSUPPORTED 2 /* head_dim != 128, n_kv_heads > 65536, or sizes whose element offsets overflow int64 */
 #define JL_ERR_WORKSPACE   3 /* decode workspace smaller than jl_bifocal_decode_workspace_size */
 #define JL_ERR_DEVICE      4 /* no HIP device, or a HIP error reported at launch              */
 

@@ -82,6 +82,7 @@ def _prefill(lib, **kw):
     (dict(scale=float("nan")), INVALID),
     (dict(d=64), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
     (dict(batch=1 << 30, n_kv=1 << 30, n_q=1 << 30, hq=1 << 20, hkv=1 << 20), UNSUPPORTED),
+    (dict(hq=65537, hkv=65537), UNSUPPORTED),   # 64 key rows of the head stride exceed a 32-bit buffer range
 ])
 def test_prefill_rejects_bad_arguments(lib, kw, status):
     assert _prefill(lib, **kw) == status

@@ -27,6 +27,8 @@ jl_status ok() {
   return JL_OK;
 }
 
+constexpr int32_t kMaxKvHeads = 65536;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Elements of a [b, n, h, 128] tensor, or -1 on int64 overflow.
@@ -68,6 +70,9 @@ jl_status check_shape(const Shape& s) {
   if (s.n_q > s.n_kv) return fail(JL_ERR_INVALID_ARG, "n_q (%d) > n_kv (%d)", s.n_q, s.n_kv);
   if (s.hq % s.hkv) return fail(JL_ERR_INVALID_ARG, "n_q_heads (%d) %% n_kv_heads (%d) != 0", s.hq, s.hkv);
   if (s.head_dim != 128) return fail(JL_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", s.head_dim);
+  // 64 key rows of one head stride must stay within a 32-bit buffer range
+  if (s.hkv > kMaxKvHeads)
+    return fail(JL_ERR_UNSUPPORTED, "n_kv_heads %d unsupported (at most %d)", s.hkv, kMaxKvHeads);
   if (elements(s.batch, s.n_q, s.hq) < 0 || elements(s.batch, s.n_kv, s.hkv) < 0)
     return fail(JL_ERR_UNSUPPORTED, "tensor sizes overflow 64-bit element offsets");
   return JL_OK;

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
       if (j0 + 16 * h + i >= we) s[i] = -INFINITY;
       mloc = fmaxf(mloc, s[i]);
     }
-    mloc = fmaxf(mloc, swap_halves(mloc));
+    mloc = half_max(mloc);
     if (__builtin_amdgcn_ballot_w64(mloc > m_run + thr)) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     for (int i2 = 0; i2 < 8; ++i2) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i2], a.scale_log2, mc));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i2 + 1], a.scale_log2, mc));
-      psum += p0 + p1;
       pk[i2] = pack_bf16(p0, p1);
+      psum = add_bf16_pair(pk[i2], psum);
     }
     l_run += psum;
     // O^T += V^T P^T: keys 16h + 8half + e
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
   process(3, kb, 1, false);
 
   // ---- merge the four waves' partial softmaxes of this chunk ----
-  const float lt = l_run + swap_halves(l_run);
+  const float lt = half_sum(l_run);
   __syncthreads();  // every wave is done with its V buffers
   float* red = reinterpret_cast<float*>(&s_v0[0][0]);  // [wave][G][D] fp32 (32 KB)
   if (n < a.grp) {

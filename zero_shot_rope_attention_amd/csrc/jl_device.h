@@ -55,6 +55,12 @@ __device__ __forceinline__ f32x2 rot_cs(long long c, double theta_rev) {
   return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
 }
 
+// acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                         acc, false);
+}
+
 // Complex product (a.x + i a.y)(b.x + i b.y).
 __device__ __forceinline__ f32x2 cmul(f32x2 a, f32x2 b) {
   return f32x2{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x};
@@ -70,6 +76,16 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) 
 // Wait until every global load of this wave, including LDS DMA, has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// LDS byte pointer.  lds_opaque() pins a per-lane LDS address in a VGPR as an
+// opaque value, so that the reads made from it keep their constant parts in
+// the instructions' offset field instead of re-adding the lane part per read.
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+__device__ __forceinline__ const lds_byte* lds_ptr(const void* generic) { return (const lds_byte*)generic; }
+__device__ __forceinline__ const lds_byte* lds_opaque(const lds_byte* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 8 bytes read by lanes 4e + i / 4 of the group, e = 0..3.
@@ -78,9 +94,29 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_byte* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
-// Wave-wide exchange with the lane 32 positions away (the other half-wave).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by the lane 32 positions away (the other
+// half-wave) through v_permlane32_swap, without an LDS round trip.  After the
+// swap one register holds the lower half's values in every lane and the other
+// the upper half's, so both halves compute op(lower, upper) identically.
+__device__ __forceinline__ f32x2 half_pair(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f32x2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+__device__ __forceinline__ float half_max(float x) {
+  const f32x2 p = half_pair(x);
+  return fmaxf(p.x, p.y);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const f32x2 p = half_pair(x);
+  return p.x + p.y;
+}
 
 // floor(n / g) for 0 <= n < 2^22 and 1 <= g, using a float reciprocal plus an
 // exact integer correction.

@@ -281,7 +281,7 @@ __device__ __forceinline__ void softmax_max(const float (&x)[NS][2][16], float (
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[s][kb][i]);
-    mloc = fmaxf(mloc, swap_halves(mloc));
+    mloc = half_max(mloc);
     if (__builtin_amdgcn_ballot_w64(mloc > m_run[s] + thr)) {
       const float m_new = fmaxf(m_run[s], mloc);
       const float alpha = __builtin_amdgcn_exp2f((m_run[s] - m_new) * scale_log2);
@@ -293,7 +293,9 @@ __device__ __forceinline__ void softmax_max(const float (&x)[NS][2][16], float (
   }
 }
 
-// Online softmax, second half: probabilities (bf16 pairs) and row sums.
+// Online softmax, second half: probabilities (bf16 pairs) and row sums.  The
+// sums add the bf16-rounded probabilities, the same values the P V product
+// weights the rows of V with, so the normalised weights sum to one.
 template <int NS>
 __device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const float (&m_run)[NS],
                                             float (&l_run)[NS], float scale_log2, uint32_t (&pk)[NS][2][8]) {
@@ -307,8 +309,8 @@ __device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const f
       for (int i2 = 0; i2 < 8; ++i2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[s][kb][2 * i2], scale_log2, mc));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[s][kb][2 * i2 + 1], scale_log2, mc));
-        psum += p0 + p1;
         pk[s][kb][i2] = pack_bf16(p0, p1);
+        psum = add_bf16_pair(pk[s][kb][i2], psum);
       }
     }
     l_run[s] += psum;
@@ -325,13 +327,16 @@ __device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const f
 template <int NS>
 __device__ __forceinline__ void pv_tile(const uint8_t* sv, const LaneOffsets& lo, const uint32_t (&pk)[NS][2][8],
                                         f32x16 (&acc)[NS][4]) {
+  const lds_byte* vp[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) vp[nb] = lds_opaque(lds_ptr(sv) + lo.v[nb]);
 #pragma unroll
   for (int step = 0; step < 4; ++step) {
     const int kb = step >> 1, half = step & 1;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const u32x2 t0 = lds_read_tr16(sv + lo.v[nb] + (32 * kb + 8 * half) * 256);
-      const u32x2 t1 = lds_read_tr16(sv + lo.v[nb] + (32 * kb + 8 * half + 4) * 256);
+      const u32x2 t0 = lds_read_tr16(vp[nb] + (32 * kb + 8 * half) * 256);
+      const u32x2 t1 = lds_read_tr16(vp[nb] + (32 * kb + 8 * half + 4) * 256);
       const u32x4 vf = {t0.x, t0.y, t1.x, t1.y};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
   if (!row_ok) return;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float lt = l_run[s] + swap_halves(l_run[s]);
+    const float lt = half_sum(l_run[s]);
     const bool empty = !(lt > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / lt;
     const float lse_v = empty ? -INFINITY : (m_run[s] * a.scale_log2 + __builtin_log2f(lt)) * kLn2;
@@ -647,19 +652,42 @@ struct HalfTile {
   u32x4 klo, khi, v0, v1;
 };
 
+// Staging loads go through buffer resources built per tile (scalar registers:
+// base = key j0 of this head, range = the keys that exist), so each lane only
+// keeps constant byte offsets and rows past n_kv read as zeros (finite, and
+// their probabilities are exactly zero).  The range check covers the VGPR
+// offset plus the instruction offset but not the scalar offset, so every row
+// offset is carried in a VGPR.
+struct StageOffsets {
+  uint32_t k;   // K item: key kt, chunk c (and c + 8 at +128 bytes)
+  uint32_t v0;  // V chunk of row `row`
+  uint32_t v1;  // the same chunk of row + 16
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(int64_t kv_rs, int half, int gtid) {
+  StageOffsets o;
+  const uint32_t row_bytes = (uint32_t)(kv_rs * 2);
+  o.k = (uint32_t)(32 * half + half_tile_key(gtid)) * row_bytes + 16u * (uint32_t)half_tile_chunk(gtid);
+  o.v0 = (uint32_t)(32 * half + (gtid >> 4)) * row_bytes + 16u * (uint32_t)(gtid & 15);
+  o.v1 = o.v0 + 16u * row_bytes;
+  return o;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* head_base, int64_t kv_rs, int n_kv,
+                                                            int j0) {
+  const int rows = min(kBN, n_kv - j0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + (int64_t)j0 * kv_rs), (short)0,
+                                           (int)(rows * kv_rs * 2), 0x00020000);
+}
+
 __device__ __forceinline__ void load_half(HalfTile& r, const uint16_t* kbase, const uint16_t* vbase, int64_t kv_rs,
-                                          int n_kv, int j0, int half, int gtid) {
-  {
-    const int kt = 32 * half + half_tile_key(gtid), c = half_tile_chunk(gtid);
-    const uint16_t* kp = kbase + (int64_t)min(j0 + kt, n_kv - 1) * kv_rs + 8 * c;
-    r.klo = *reinterpret_cast<const u32x4*>(kp);
-    r.khi = *reinterpret_cast<const u32x4*>(kp + kHalfD);
-  }
-  {
-    const int row = 32 * half + (gtid >> 4), c = gtid & 15;
-    r.v0 = *reinterpret_cast<const u32x4*>(vbase + (int64_t)min(j0 + row, n_kv - 1) * kv_rs + 8 * c);
-    r.v1 = *reinterpret_cast<const u32x4*>(vbase + (int64_t)min(j0 + row + 16, n_kv - 1) * kv_rs + 8 * c);
-  }
+                                          int n_kv, int j0, const StageOffsets& so) {
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, kv_rs, n_kv, j0);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, kv_rs, n_kv, j0);
+  r.klo = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k, 0, 0);
+  r.khi = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k + 128, 0, 0);
+  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(rv, so.v0, 0, 0);
+  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rv, so.v1, 0, 0);
 }
 
 template <bool kGrouped>
@@ -715,11 +743,14 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
   auto read_k = [&](int i) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(kbuf + lo.k[i >> 1] + (i & 1) * (32 * 256));
   };
+  const lds_byte* vp[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) vp[nb] = kPV ? lds_opaque(lds_ptr(vbuf) + lo.v[nb]) : nullptr;
   auto read_v = [&](int i) -> u32x4 {
     const int st = i >> 2, nb = i & 3;
     const int kb = st >> 1, half = st & 1;
-    const u32x2 t0 = lds_read_tr16(vbuf + lo.v[nb] + (32 * kb + 8 * half) * 256);
-    const u32x2 t1 = lds_read_tr16(vbuf + lo.v[nb] + (32 * kb + 8 * half + 4) * 256);
+    const u32x2 t0 = lds_read_tr16(vp[nb] + (32 * kb + 8 * half) * 256);
+    const u32x2 t1 = lds_read_tr16(vp[nb] + (32 * kb + 8 * half + 4) * 256);
     return u32x4{t0.x, t0.y, t1.x, t1.y};
   };
   u32x4 kr[kDist + 1], vr[kDist + 1];
@@ -815,7 +846,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
   }
   HalfTile regs;
-  load_half(regs, kbase, vbase, kv_rs, a.n_kv, 0, grp, gtid);
+  const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
+  load_half(regs, kbase, vbase, kv_rs, a.n_kv, 0, soff);
 
   bf16x8 qf[8];
   bf16x8 qg[8];
@@ -878,7 +910,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       if (gtid < 64) base_angles(1, 2 * grp);
       __syncthreads();
     }
-    load_half(regs, kbase, vbase, kv_rs, a.n_kv, kBN, grp, gtid);
+    load_half(regs, kbase, vbase, kv_rs, a.n_kv, kBN, soff);
     store(1, 2 * grp);
   }
   if constexpr (kGrouped) {
@@ -924,7 +956,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     constexpr int kKind = decltype(kind_tag)::value;
     const int tt = k + ahead;
     const bool do_stage = tt < ntiles && tt >= 2;
-    if (do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, grp, gtid);
+    // plain: the staging loads fly during the MFMA phase; bifocal: they are
+    // issued at the start of the VALU phase, so that the 16 registers they fill
+    // are not live across the MFMA phase, where the bifocal kernel has none left
+    if (!kGrouped && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
     // V of tile k-1 (at k = 0 the probabilities are zero and tile 0's finite V
@@ -951,6 +986,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
     }
     __syncthreads();
+    if (kGrouped && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
@@ -995,7 +1031,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 
   // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
   if (!row_ok) return;
-  const float lt = l_run[0] + swap_halves(l_run[0]);
+  const float lt = half_sum(l_run[0]);
   const float inv = 1.0f / lt;
   const float lse_v = (m_run[0] * a.scale_log2 + __builtin_log2f(lt)) * kLn2;
   uint16_t* o = a.out + (((int64_t)b * a.n_q + my_row) * a.hq + hq) * kD;
