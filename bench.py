@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the bifocal-attention hot path on one MI355X.
 
-A step is one pass of the whole path over one synthetic batch: the fused
-bifocal prefill of the prompt (g(s), on-the-fly correction, the three-pass
-merge) followed by one bifocal decode step of the next token against the
-resulting cache (split-K kernel + combine).  The default workload is the
+A step is one pass of the whole path over one synthetic batch: the bifocal
+prefill of the prompt (g(s), the correction rotation, the three-pass merge) --
+timed in its two-launch form, an elementwise pass that writes the corrected keys
+to a workspace followed by the attention kernel -- then one bifocal decode step
+of the next token against the resulting cache (split-K kernel + combine).  The
+single-kernel form, which corrects every key tile inside the attention kernel,
+is timed next to it.  The default workload is the
 Qwen3-8B-shaped attention layer at 128K: batch 1, 32 query / 8 KV heads,
 head_dim 128, seq 131072, pretrained window 32768, local window 4096, RoPE base
 1e6 (g = 4), bf16 N(0,1) inputs from a fixed seed.
@@ -126,11 +129,12 @@ def main():
     q_dec = q[:, -1:].contiguous()
     out_dec = torch.empty_like(q_dec)
     ws = torch.empty(jl.jl_bifocal_decode_workspace_size(b, s, hq, hkv), dtype=torch.uint8, device=dev)
+    ws_pre = torch.empty(jl.jl_bifocal_prefill_workspace_size(b, s, hkv), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev):
         ev[0].record(stream)
-        jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
+        jl.jl_bifocal_prefill_ws(q, k, v, out, lse, big_l, w, base, ws_pre)
         ev[1].record(stream)
         jl.jl_bifocal_decode(q_dec, k, v, out_dec, None, big_l, w, base, ws)
         ev[2].record(stream)
@@ -173,13 +177,28 @@ def main():
                    "group_factor": g},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_pp_kernel<1> (bifocal)", "flops_per_launch": flops,
-                     "avg_launch_ms": round(pre_avg, 4)},
+                     "kernel": "prefill_pp_kernel<3> (bifocal, corrected keys staged) + correct_keys_kernel",
+                     "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
+                     "timing": "HIP events around the whole prefill call (both launches) on its stream"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
         "decode_in_step_us": round(float(np.mean(dec_ms)) * 1e3, 2),
     }
 
     if not args.no_extras:
+        # single-kernel bifocal prefill (keys corrected tile by tile in the kernel)
+        for _ in range(2):
+            jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        result["fused_prefill"] = {"ms": round(fused_ms, 4), "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                                   "kernel": "prefill_pp_kernel<1>", "over_two_launch_time": round(fused_ms / pre_avg, 4)}
+        log(f"single-kernel bifocal prefill {fused_ms:.2f} ms")
+
         # plain causal prefill built the same way (same numerator)
         out_p = torch.empty_like(q)
         for _ in range(2):

@@ -67,7 +67,7 @@ typedef int32_t jl_status;
 #define JL_ERR_INVALID_ARG 1 /* null/misaligned pointer, size < 1, n_q > n_kv, Hq % Hkv != 0,
                                 L < 1, W < 1, W > L, rope_base <= 1 or not finite            */
 #define JL_ERR_UNSUPPORTED 2 /* head_dim != 128, n_kv_heads > 65536, or sizes whose element offsets overflow int64 */
-#define JL_ERR_WORKSPACE   3 /* decode workspace smaller than jl_bifocal_decode_workspace_size */
+#define JL_ERR_WORKSPACE   3 /* workspace smaller than the matching *_workspace_size result    */
 #define JL_ERR_DEVICE      4 /* no HIP device, or a HIP error reported at launch              */
 
 /* Message for the last non-OK status on this thread ("" if none). */
@@ -94,6 +94,31 @@ jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* 
                              int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
                              int64_t local_window, double rope_base, float softmax_scale,
                              void* stream);
+
+/* Bytes of device workspace jl_bifocal_prefill_ws needs: one corrected copy of
+ * the keys, bf16 [B, n_kv, Hkv, D].  0 for invalid sizes. */
+size_t jl_bifocal_prefill_workspace_size(int32_t batch, int32_t n_kv, int32_t n_kv_heads, int32_t head_dim);
+
+/* Same result as jl_bifocal_prefill (same arguments, layouts and rounding of the
+ * corrected keys) computed in two launches: an elementwise pass first writes
+ * k^g_j = rot(k_j, c(j) theta) for every cached key to `workspace` (bf16,
+ * layout of k), then the attention kernel stages those corrected keys like
+ * plain keys instead of rotating every key tile once per query block.  The
+ * cache itself is not modified.  The pages fuse the correction into the one
+ * attention kernel (Jet-Long summary page: a single fused kernel, no extra
+ * pass); on this GPU the extra pass is cheaper than repeating the rotation per
+ * query block, so this entry point trades workspace for speed.
+ *   workspace       : device memory, 16-byte aligned, owned by the caller; it
+ *                     may be NULL when g(n_kv) == 1 (the plain path needs none),
+ *                     otherwise NULL or misaligned is JL_ERR_INVALID_ARG
+ *   workspace_bytes : >= jl_bifocal_prefill_workspace_size(...), else
+ *                     JL_ERR_WORKSPACE
+ * The workspace contents are scratch: overwritten by every call. */
+jl_status jl_bifocal_prefill_ws(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                int64_t local_window, double rope_base, float softmax_scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Plain causal RoPE attention built with the same kernel skeleton (the base
  * model; denominator of the "overhead vs plain" and "vs plain causal"

@@ -128,6 +128,32 @@ def test_decode_workspace_and_validation(lib):
     assert dec(d=96, wsb=need) == UNSUPPORTED
 
 
+def test_prefill_ws_workspace_and_validation(lib):
+    # one corrected copy of the keys: B * n_kv * Hkv * 128 bf16
+    assert lib.jl_bifocal_prefill_workspace_size(1, 131072, 8, 128) == 131072 * 8 * 128 * 2
+    assert lib.jl_bifocal_prefill_workspace_size(2, 100, 3, 128) == 2 * 100 * 3 * 128 * 2
+    assert lib.jl_bifocal_prefill_workspace_size(1, 100, 2, 64) == 0
+    assert lib.jl_bifocal_prefill_workspace_size(0, 100, 2, 128) == 0
+
+    def pre(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, batch=1, n_q=64, n_kv=64, hq=4, hkv=2, d=128,
+                 big_l=32, w=8, base=1e4, scale=0.0, ws=FAKE, wsb=64 * 2 * 128 * 2)
+        a.update(kw)
+        return lib.jl_bifocal_prefill_ws(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["n_q"],
+                                         a["n_kv"], a["hq"], a["hkv"], a["d"], a["big_l"], a["w"], a["base"],
+                                         a["scale"], a["ws"], a["wsb"], None)
+
+    need = lib.jl_bifocal_prefill_workspace_size(1, 64, 2, 128)
+    assert pre(wsb=need - 1) == WORKSPACE          # g = 2 needs the corrected keys
+    assert pre(ws=None) == INVALID
+    assert pre(ws=FAKE + 8) == INVALID             # misaligned
+    assert pre(d=64) == UNSUPPORTED
+    assert pre(w=33) == INVALID
+    if not _has_gpu():
+        assert pre() == DEVICE                     # arguments fine, no device here
+        assert pre(big_l=64, ws=None, wsb=0) == DEVICE   # g = 1: no workspace needed
+
+
 def test_error_message_cleared_on_success_path_is_thread_local(lib):
     import threading
     assert _prefill(lib, w=0) == INVALID

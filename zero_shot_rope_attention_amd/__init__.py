@@ -20,6 +20,8 @@ __all__ = [
     "load_library",
     "jl_group_factor",
     "jl_bifocal_prefill",
+    "jl_bifocal_prefill_workspace_size",
+    "jl_bifocal_prefill_ws",
     "jl_plain_prefill",
     "jl_bifocal_prefill_passes",
     "jl_bifocal_decode_workspace_size",
@@ -38,6 +40,9 @@ _SIGNATURES = {
     "jl_group_factor": (_i64, [_i64, _i64]),
     "jl_bifocal_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
                                   _f32, _vp]),
+    "jl_bifocal_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "jl_bifocal_prefill_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
+                                     _f32, _vp, _sz, _vp]),
     "jl_plain_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "jl_bifocal_prefill_passes": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
                                          _f64, _f32, _vp]),
@@ -107,6 +112,22 @@ def jl_bifocal_prefill(q, k, v, out, lse, pretrained_window, local_window, rope_
     _check(load_library().jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq,
                                              hkv, d, int(pretrained_window), int(local_window), float(rope_base),
                                              float(softmax_scale), _stream(stream)))
+
+
+def jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim=128) -> int:
+    return int(load_library().jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim))
+
+
+def jl_bifocal_prefill_ws(q, k, v, out, lse, pretrained_window, local_window, rope_base, workspace,
+                          softmax_scale=0.0, stream=None):
+    """As jl_bifocal_prefill, with the corrected keys written to `workspace` (a device
+    tensor of at least jl_bifocal_prefill_workspace_size bytes) by a pass of their own."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_prefill_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq,
+                                                hkv, d, int(pretrained_window), int(local_window), float(rope_base),
+                                                float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def jl_plain_prefill(q, k, v, out, lse, softmax_scale=0.0, stream=None):

@@ -137,8 +137,8 @@ jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* ou
   JL_TRY(check_pointer(out, "out"));
   JL_TRY(check_pointer(lse, "lse", true));
   JL_TRY(device_check());
-  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, 1, 2.0,
-                       scale};
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, 1,
+                       2.0, scale};
   return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -156,8 +156,8 @@ jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* 
   const int64_t g = jl_group_factor(n_kv, pretrained_window);
   const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
   const jl::PrefillMode mode = g == 1 ? jl::kModePlain : jl::kModeBifocal;
-  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, (int32_t)g, w,
-                       rope_base, scale};
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads,
+                       (int32_t)g, w, rope_base, scale};
   return launched(jl::launch_prefill(mode, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -174,9 +174,41 @@ jl_status jl_bifocal_prefill_passes(const void* q, const void* k, const void* v,
   JL_TRY(device_check());
   const int64_t g = jl_group_factor(n_kv, pretrained_window);
   const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
-  jl::PrefillProblem p{q, k, v, nullptr, nullptr, out_abc, lse_abc, batch, n_q, n_kv, n_q_heads, n_kv_heads,
-                       (int32_t)g, w, rope_base, scale};
+  jl::PrefillProblem p{q, k, v, nullptr, nullptr, out_abc, lse_abc, nullptr, batch, n_q, n_kv, n_q_heads,
+                       n_kv_heads, (int32_t)g, w, rope_base, scale};
   return launched(jl::launch_prefill(jl::kModePasses, p, static_cast<hipStream_t>(stream)));
+}
+
+size_t jl_bifocal_prefill_workspace_size(int32_t batch, int32_t n_kv, int32_t n_kv_heads, int32_t head_dim) {
+  if (batch < 1 || n_kv < 1 || n_kv_heads < 1 || head_dim != 128) return 0;
+  const int64_t e = elements(batch, n_kv, n_kv_heads);
+  if (e < 0) return 0;
+  return (size_t)e * 2;
+}
+
+jl_status jl_bifocal_prefill_ws(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
+                                int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                int64_t pretrained_window, int64_t local_window, double rope_base,
+                                float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  const int64_t g = jl_group_factor(n_kv, pretrained_window);
+  if (g > 1) {
+    JL_TRY(check_pointer(workspace, "workspace"));
+    const size_t need = jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim);
+    if (workspace_bytes < need)
+      return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  }
+  JL_TRY(device_check());
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  const jl::PrefillMode mode = g == 1 ? jl::kModePlain : jl::kModeBifocalPre;
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, g == 1 ? nullptr : workspace, batch, n_q, n_kv,
+                       n_q_heads, n_kv_heads, (int32_t)g, w, rope_base, scale};
+  return launched(jl::launch_prefill(mode, p, static_cast<hipStream_t>(stream)));
 }
 
 size_t jl_bifocal_decode_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,

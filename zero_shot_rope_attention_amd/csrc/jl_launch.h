@@ -7,7 +7,10 @@
 
 namespace jl {
 
-enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2 };
+// kModeBifocal corrects the keys tile by tile inside the attention kernel;
+// kModeBifocalPre first writes the corrected keys of the whole cache to a
+// workspace (one elementwise pass) and stages them like plain keys.
+enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2, kModeBifocalPre = 3 };
 
 // Everything a prefill launch needs; validated by the caller.
 struct PrefillProblem {
@@ -18,6 +21,7 @@ struct PrefillProblem {
   float* lse;       // fp32 [B, Hq, n_q] or null  (plain / bifocal)
   float* out_abc;   // fp32 [3, B, n_q, Hq, D]    (passes)
   float* lse_abc;   // fp32 [3, B, Hq, n_q]       (passes)
+  void* kg;         // bf16 [B, n_kv, Hkv, D] corrected keys (bifocal, precorrected)
   int32_t batch, n_q, n_kv, n_q_heads, n_kv_heads;
   int32_t group;         // g(s); 1 for plain
   int32_t local_window;  // W, already clamped to <= n_kv

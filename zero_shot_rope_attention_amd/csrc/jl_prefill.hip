@@ -45,6 +45,7 @@ struct PrefillArgs {
   float* lse;
   float* out_abc;
   float* lse_abc;
+  const uint16_t* kg;  // corrected keys of the whole cache (precorrected mode)
   int32_t batch, n_q, n_kv, hq, hkv;
   int32_t grp;        // Hq / Hkv
   int32_t hpw;        // query heads per workgroup
@@ -690,6 +691,18 @@ __device__ __forceinline__ void load_half(HalfTile& r, const uint16_t* kbase, co
   r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rv, so.v1, 0, 0);
 }
 
+__device__ __forceinline__ void load_k_only(HalfTile& r, const uint16_t* kbase, int64_t kv_rs, int n_kv, int j0,
+                                            const StageOffsets& so) {
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, kv_rs, n_kv, j0);
+  r.klo = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k, 0, 0);
+  r.khi = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k + 128, 0, 0);
+}
+__device__ __forceinline__ void store_k_only(const HalfTile& r, uint8_t* sk, int half, int gtid) {
+  const int kt = 32 * half + half_tile_key(gtid), c = half_tile_chunk(gtid);
+  *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c) << 4)) = r.klo;
+  *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c + 8) << 4)) = r.khi;
+}
+
 template <bool kGrouped>
 __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8_t* skg, uint8_t* sv,
                                            const f32x2* s_tdelta, const f32x2* base, int j0, int g, float inv_g,
@@ -784,15 +797,18 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
 
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
-  static_assert(MODE == kModePlain || MODE == kModeBifocal, "ping-pong kernel: plain or bifocal");
-  constexpr bool kGrouped = MODE == kModeBifocal;
+  static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre,
+                "ping-pong kernel: plain or bifocal");
+  constexpr bool kGrouped = MODE != kModePlain;     // grouped scores on remote keys
+  constexpr bool kRotate = MODE == kModeBifocal;    // keys corrected here, tile by tile
+  constexpr bool kPre = MODE == kModeBifocalPre;    // keys corrected beforehand (a.kg)
   constexpr int kTileBytes = kBN * 256;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];                  // K as cached
   __shared__ __attribute__((aligned(16))) uint8_t s_kg[kGrouped ? 2 * kTileBytes : 16];  // corrected K
   __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];                  // V row-major
-  __shared__ f32x2 s_tdelta[kGrouped ? 64 * kTdStride : 1];  // E(-u theta_d), u = 0..63, padded rows
-  __shared__ f32x2 s_base[kGrouped ? 4 * kHalfD : 1];     // E(c(j0) theta_d): [group][parity of k]
+  __shared__ f32x2 s_tdelta[kRotate ? 64 * kTdStride : 1];  // E(-u theta_d), u = 0..63, padded rows
+  __shared__ f32x2 s_base[kRotate ? 4 * kHalfD : 1];     // E(c(j0) theta_d): [group][parity of k]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -838,16 +854,34 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   const int64_t kv_rs = (int64_t)a.hkv * kD;
   const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
   const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+  const uint16_t* kgbase = kPre ? a.kg + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD : nullptr;
+
+  // tile kinds of this workgroup's rows [p0, p1] (see the tile program below)
+  const int p0_wg = pos_off + row0_wg;
+  int n_interior = 0;
+  if constexpr (MODE == kModePlain) n_interior = min(ntiles, max(0, (p0_wg + 1) / kBN));
+  if constexpr (kGrouped) n_interior = min(ntiles, max(0, (p0_wg - a.w + 1) / kBN));
+  // first tile whose causal keys are local for every row of the workgroup
+  int t_local = n_interior;
+  if constexpr (kGrouped) {
+    const int first_all_local = pos_off + last_row_wg - a.w + 1;
+    t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
+    t_local = min(ntiles, max(n_interior, t_local));
+  }
+  // precorrected mode: interior tiles stage the corrected keys (into s_kg) in
+  // place of the cached ones, edge tiles both, local tiles the cached ones
+  auto k_src = [&](int t) { return (kPre && t < n_interior) ? kgbase : kbase; };
+  auto k_dst = [&](int t) { return ((kPre && t < n_interior) ? s_kg : s_k) + (t & 1) * kTileBytes; };
 
   // rotation table first, while few values are live
-  if constexpr (kGrouped) {
+  if constexpr (kRotate) {
 #pragma unroll 1
     for (int idx = tid; idx < 64 * kHalfD; idx += 512)
       s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
   }
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
-  load_half(regs, kbase, vbase, kv_rs, a.n_kv, 0, soff);
+  load_half(regs, k_src(0), vbase, kv_rs, a.n_kv, 0, soff);
 
   bf16x8 qf[8];
   bf16x8 qg[8];
@@ -889,15 +923,25 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     s_base[slot * kHalfD + (gtid & 63)] = rot_cs((long long)(j / a.g) - j, a.theta_rev[gtid & 63]);
   };
   auto store = [&](int tt, int slot) {  // slot: rotation-base slot
-    store_half<kGrouped>(regs, s_k + (tt & 1) * kTileBytes, s_kg + (kGrouped ? (tt & 1) * kTileBytes : 0),
-                         s_v + (tt % 3) * kTileBytes, s_tdelta, s_base + (kGrouped ? slot * kHalfD : 0), tt * kBN,
-                         a.g, a.inv_g, grp, gtid);
+    if constexpr (kPre) {
+      store_half<false>(regs, k_dst(tt), nullptr, s_v + (tt % 3) * kTileBytes, nullptr, nullptr, 0, 1, 1.0f, grp,
+                        gtid);
+      if (tt >= n_interior && tt < t_local) {  // edge tile: the corrected keys too
+        HalfTile kgr;
+        load_k_only(kgr, kgbase, kv_rs, a.n_kv, tt * kBN, soff);
+        store_k_only(kgr, s_kg + (tt & 1) * kTileBytes, grp, gtid);
+      }
+    } else {
+      store_half<kRotate>(regs, s_k + (tt & 1) * kTileBytes, s_kg + (kRotate ? (tt & 1) * kTileBytes : 0),
+                          s_v + (tt % 3) * kTileBytes, s_tdelta, s_base + (kRotate ? slot * kHalfD : 0), tt * kBN,
+                          a.g, a.inv_g, grp, gtid);
+    }
   };
 
   // ---- prologue: tiles 0 and 1, each group its half ----
   // s_base slot [grp][k & 1] holds the rotation base of the tile group grp
   // stages in V(k); the prologue borrows slot [grp][0] for tiles 0 and 1.
-  if constexpr (kGrouped) {
+  if constexpr (kRotate) {
     if (gtid < 64) {
       s_base[(2 * grp) * kHalfD + gtid] = rot_cs(0, a.theta_rev[gtid]);  // tile 0: c(0) = 0
     }
@@ -906,14 +950,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   store(0, 2 * grp);
   __syncthreads();
   if (ntiles > 1) {
-    if constexpr (kGrouped) {
+    if constexpr (kRotate) {
       if (gtid < 64) base_angles(1, 2 * grp);
       __syncthreads();
     }
-    load_half(regs, kbase, vbase, kv_rs, a.n_kv, kBN, soff);
+    load_half(regs, k_src(1), vbase, kv_rs, a.n_kv, kBN, soff);
     store(1, 2 * grp);
   }
-  if constexpr (kGrouped) {
+  if constexpr (kRotate) {
     __syncthreads();
     // slot [grp][k & 1] holds the base of the tile staged in V(k): the first
     // in-loop stagings are V(1) (group A, tile 2) and V(0) (group B, tile 2)
@@ -928,10 +972,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[0][nb] = f32x16{};
 
-  const int p0_wg = pos_off + row0_wg;
-  int n_interior = 0;
-  if constexpr (MODE == kModePlain) n_interior = min(ntiles, max(0, (p0_wg + 1) / kBN));
-  if constexpr (MODE == kModeBifocal) n_interior = min(ntiles, max(0, (p0_wg - a.w + 1) / kBN));
   auto uses = [&](int t) { return wave_rows && t * kBN <= wp_hi; };
 
   float xs[1][2][16];
@@ -954,12 +994,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
   auto tile = [&](int k, auto kind_tag) {
     constexpr int kKind = decltype(kind_tag)::value;
+    // the wave in its MFMA phase goes first when both waves of a SIMD can issue
+    __builtin_amdgcn_s_setprio(2);
     const int tt = k + ahead;
     const bool do_stage = tt < ntiles && tt >= 2;
     // plain: the staging loads fly during the MFMA phase; bifocal: they are
     // issued at the start of the VALU phase, so that the 16 registers they fill
     // are not live across the MFMA phase, where the bifocal kernel has none left
-    if (!kGrouped && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
+    if (!kRotate && do_stage) load_half(regs, k_src(tt), vbase, kv_rs, a.n_kv, tt * kBN, soff);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
     // V of tile k-1 (at k = 0 the probabilities are zero and tile 0's finite V
@@ -978,7 +1020,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
         if constexpr (kKind == kEdge) {
           const bool use_grp = (j0 <= wp_hi - a.w);
           const bool use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);
-          tile_scores<MODE, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
+          tile_scores<kModeBifocal, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
         } else {
           tile_scores<kModePlain, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, true, false, xs);
         }
@@ -986,7 +1028,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
     }
     __syncthreads();
-    if (kGrouped && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
+    __builtin_amdgcn_s_setprio(0);
+    if (kRotate && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
@@ -1001,23 +1044,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       else
         store(tt, 2 * grp + (k & 1));
     }
-    if constexpr (kGrouped && kKind != kLocal) {
+    if constexpr (kRotate && kKind != kLocal) {
       // base of the tile this group stages in V(k+1), into the other slot
       if (gtid < 64) base_angles(tt + 1, 2 * grp + ((k + 1) & 1));
     }
     __syncthreads();
   };
 
-  // first tile whose causal keys are local for every row of the workgroup
-  int t_local = n_interior;
-  if constexpr (MODE == kModeBifocal) {
-    const int first_all_local = pos_off + last_row_wg - a.w + 1;
-    t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
-    t_local = min(ntiles, max(n_interior, t_local));
-  }
   int k = 0;
   for (; k < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{});
-  if constexpr (MODE == kModeBifocal) {
+  if constexpr (kGrouped) {
     // the base-RoPE query fragment is only needed from the band on
     const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
 #pragma unroll
@@ -1046,6 +1082,52 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   if (a.lse && h == 0) a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = lse_v;
 }
 
+// ---------------------------------------------------------------------------
+// Corrected keys of the whole cache, for the precorrected mode:
+// k^g_j = rot(k_j, c(j) theta), c(j) = floor(j / g) - j, written in the layout
+// of k.  Thread (row, c) handles rotate-half pairs 8c .. 8c+7 of one cached key
+// row for every KV head: the 8 angles are reduced in fp64 once and reused.
+// ---------------------------------------------------------------------------
+struct CorrectArgs {
+  const uint16_t* k;
+  uint16_t* kg;
+  int64_t rows;  // batch * n_kv
+  int32_t n_kv, hkv, g;
+  double theta_rev[kHalfD];
+};
+
+__global__ __launch_bounds__(256) void correct_keys_kernel(const CorrectArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int c = threadIdx.x & 7;
+  if (row >= a.rows) return;
+  const int j = (int)(row % a.n_kv);
+  const long long cj = (long long)(j / a.g) - j;
+  f32x2 cs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cs[e] = rot_cs(cj, a.theta_rev[8 * c + e]);
+  for (int hh = 0; hh < a.hkv; ++hh) {
+    const int64_t base = (row * a.hkv + hh) * kD + 8 * c;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(a.k + base);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(a.k + base + kHalfD);
+    u32x4 glo, ghi;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      float y1[2], y2[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int e = 2 * e2 + q2;
+        const float x1 = elem(lo, e), x2 = elem(hi, e);
+        y1[q2] = x1 * cs[e].x - x2 * cs[e].y;
+        y2[q2] = x2 * cs[e].x + x1 * cs[e].y;
+      }
+      glo[e2] = pack_bf16(y1[0], y1[1]);
+      ghi[e2] = pack_bf16(y2[0], y2[1]);
+    }
+    *reinterpret_cast<u32x4*>(a.kg + base) = glo;
+    *reinterpret_cast<u32x4*>(a.kg + base + kHalfD) = ghi;
+  }
+}
+
 template <int MODE, int NW>
 hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   PrefillArgs a;
@@ -1056,6 +1138,7 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   a.lse = p.lse;
   a.out_abc = p.out_abc;
   a.lse_abc = p.lse_abc;
+  a.kg = static_cast<const uint16_t*>(p.kg);
   a.batch = p.batch;
   a.n_q = p.n_q;
   a.n_kv = p.n_kv;
@@ -1081,6 +1164,19 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   const long long blocks = (long long)a.n_units * a.n_qblocks;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if constexpr (MODE == kModeBifocalPre) {
+    CorrectArgs c;
+    c.k = a.k;
+    c.kg = static_cast<uint16_t*>(p.kg);
+    c.rows = (int64_t)p.batch * p.n_kv;
+    c.n_kv = p.n_kv;
+    c.hkv = p.n_kv_heads;
+    c.g = p.group;
+    for (int d = 0; d < kHalfD; ++d) c.theta_rev[d] = a.theta_rev[d];
+    const long long cblocks = (c.rows + 31) / 32;
+    if (cblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(correct_keys_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream, c);
+  }
   if constexpr (MODE == kModePasses)
     hipLaunchKernelGGL((prefill_kernel<MODE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   else
@@ -1095,6 +1191,7 @@ hipError_t launch_prefill(PrefillMode mode, const PrefillProblem& p, hipStream_t
     case kModePlain: return launch_mode<kModePlain, 8>(p, stream);
     case kModeBifocal: return launch_mode<kModeBifocal, 8>(p, stream);
     case kModePasses: return launch_mode<kModePasses, 4>(p, stream);
+    case kModeBifocalPre: return launch_mode<kModeBifocalPre, 8>(p, stream);
   }
   return hipErrorInvalidValue;
 }
