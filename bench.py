@@ -47,6 +47,38 @@ WORKLOADS = {
 }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bifocal_qwen3_8b_128k_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant prefill kernel, from the committed
+    rocprofv3 counter summary -- only while the kernel sources are the ones the
+    counters were taken on (their sha256 is recorded there); else None."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    value, hashes = None, {}
+    for ln in lines:
+        ln = ln.strip()
+        if ln.startswith("traffic_bytes_per_launch:"):
+            value = int(ln.split(":", 1)[1])
+        elif ln.startswith("source_sha256 "):
+            name, digest = ln[len("source_sha256 "):].split(":", 1)
+            hashes[name.strip()] = digest.strip()
+    if value is None or not hashes:
+        return None
+    for name, digest in hashes.items():
+        path = os.path.join(ROOT, "zero_shot_rope_attention_amd", "csrc", name)
+        try:
+            if hashlib.sha256(open(path, "rb").read()).hexdigest() != digest:
+                return None
+        except OSError:
+            return None
+    return value
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -176,10 +208,12 @@ def main():
                    "head_dim": 128, "pretrained_window": big_l, "local_window": w, "rope_base": base,
                    "group_factor": g},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "prefill_pp_kernel<3> (bifocal, corrected keys staged) + correct_keys_kernel",
                      "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
-                     "timing": "HIP events around the whole prefill call (both launches) on its stream"},
+                     "timing": "HIP events around the whole prefill call (both launches) on its stream",
+                     "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3>: rocprofv3 FETCH_SIZE x 2.0 + "
+                                     "WRITE_SIZE x 1.0 (scales from a 1 GiB copy), null if the kernel changed since"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
         "decode_in_step_us": round(float(np.mean(dec_ms)) * 1e3, 2),
     }
