@@ -998,9 +998,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     __builtin_amdgcn_s_setprio(2);
     const int tt = k + ahead;
     const bool do_stage = tt < ntiles && tt >= 2;
-    // plain: the staging loads fly during the MFMA phase; bifocal: they are
-    // issued at the start of the VALU phase, so that the 16 registers they fill
-    // are not live across the MFMA phase, where the bifocal kernel has none left
+    // plain and precorrected: the staging loads fly during the MFMA phase; fused
+    // bifocal: they are issued at the start of the VALU phase, so that the 16
+    // registers they fill are not live across the MFMA phase, where that kernel
+    // has none left
     if (!kRotate && do_stage) load_half(regs, k_src(tt), vbase, kv_rs, a.n_kv, tt * kBN, soff);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
@@ -1029,6 +1030,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     }
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
+    // the row maxima belong to this phase: left to itself the compiler hoists
+    // them above the barrier, where the MFMA wave would first wait for its last
+    // products instead of reaching the barrier as soon as they are issued (not
+    // in the precorrected kernel, whose staging registers stay live across the
+    // MFMA phase: there the longer live range costs spills in the loop)
+    if constexpr (!kPre) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xs[0][kb][i]));
+    }
     if (kRotate && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || uses(k)) {
