@@ -11,11 +11,15 @@
 // cut into chunks that never straddle s - W; every chunk yields a partial
 // (normalised output, log-sum-exp) and a second kernel merges the partials.
 //
-// Per workgroup: one KV head, its G query heads, one chunk of up to 512 keys
-// (4 waves x 128 keys).  Per wave and 32-key block:
+// Per workgroup: one KV head, its G query heads, one chunk of up to 1024 keys
+// (2 waves x 512 keys, each wave streaming its keys in 32-key blocks with the
+// next block in flight).  Two-wave workgroups, four per CU, keep the merge at
+// the end of one workgroup from idling a large share of the CU's loads.
+// Per wave and block:
 //   S^T = K Q^T   (MFMA; A = key fragments loaded straight from HBM, 16-byte
-//                  loads; remote keys are rotated by c(j) theta in registers,
-//                  each lane holding both halves of its rotate-half pairs)
+//                  loads; remote keys are rotated in registers by the
+//                  correction relative to the query's, each lane holding both
+//                  halves of its rotate-half pairs)
 //   O^T += V^T P^T (MFMA; V transposed through a per-wave LDS tile)
 #include <cmath>
 
@@ -25,8 +29,8 @@
 namespace jl {
 namespace {
 
-constexpr int kKeysPerWave = 128;
-constexpr int kWaves = 4;
+constexpr int kKeysPerWave = 512;
+constexpr int kWaves = 2;
 constexpr int kKeysPerWG = kKeysPerWave * kWaves;
 constexpr int kMaxGroup = 16;  // query heads per KV head handled by one workgroup
 
@@ -71,13 +75,15 @@ constexpr int kBlk = 32;              // keys per MFMA block
 constexpr int kVmemPerBlock = 16;     // 8 K loads + 8 V copies per block and lane
 constexpr int kVBlockBytes = kBlk * 256;
 
+// Two waves per SIMD (<= 256 VGPRs): four workgroups per CU.
 template <bool BIF>
-__global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
+    const DecodeArgs a) {
   // per-wave V blocks, double-buffered; two separate objects so that the
   // compiler can tell which direct copy a transposed read waits for
   __shared__ __attribute__((aligned(16))) uint8_t s_v0[kWaves][kVBlockBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_v1[kWaves][kVBlockBytes];
-  __shared__ float s_fb[kWaves][kHalfD];  // per wave: c(ws) theta_d / (2 pi), reduced to [-1/2, 1/2]
+  __shared__ float s_fb[kWaves][kHalfD];  // per wave: (c(ws) - c(p)) theta_d / (2 pi), reduced to [-1/2, 1/2]
   __shared__ float s_th[kWaves][kHalfD];  // theta_d / (2 pi)
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][kMaxGroup];
@@ -110,75 +116,82 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
 
   // ---- per-block loads: K fragment into registers (key j0 + perm_key(n),
   // d = 16kk + 8h + e), V rows into this wave's LDS buffer by direct copies ----
+  // Each block builds buffer resources over the (at most 32) rows it may
+  // touch, from jb = its first row clamped into the wave's range; rows past the
+  // range re-read the wave's last key (we - 1 >= ks always), so every offset
+  // stays below 32 rows.  Buffer (MUBUF) loads rather than FLAT ones: while a
+  // FLAT-encoded LDS copy is in flight the compiler can only wait for every
+  // load, never for the older ones alone.
+  const uint32_t row_bytes = (uint32_t)kv_rs * 2u;  // <= 16 MiB (n_kv_heads <= 65536)
+  typedef __attribute__((address_space(3))) void lds_void;
   auto issue = [&](int blk, u32x4 (&kr)[8], int buf) {
     const int j0 = ws + blk * kBlk;
-    const uint16_t* kp = kbase + (int64_t)min(j0 + perm_key(n), we - 1) * kv_rs + 8 * h;  // we >= 1
+    const int jb = min(j0, we - 1);
+    const uint32_t nbytes = (uint32_t)min(kBlk, we - jb) * row_bytes;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
+    const uint32_t ko = (uint32_t)(min(j0 + perm_key(n), we - 1) - jb) * row_bytes + 16u * (uint32_t)h;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kr[kk] = *reinterpret_cast<const u32x4*>(kp + 16 * kk);
+    for (int kk = 0; kk < 8; ++kk) kr[kk] = __builtin_amdgcn_raw_buffer_load_b128(krs, ko + 32u * kk, 0, 0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 4 * r + (lane >> 4);
       const int c = v_chunk(row, lane & 15);
-      lds_dma16(vbase + (int64_t)min(j0 + row, we - 1) * kv_rs + 8 * c,
-                buf ? &s_v1[wave][r * 1024] : &s_v0[wave][r * 1024]);
+      const uint32_t vo = (uint32_t)(min(j0 + row, we - 1) - jb) * row_bytes + 16u * (uint32_t)c;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf ? &s_v1[wave][r * 1024] : &s_v0[wave][r * 1024]),
+                                               16, (int)vo, 0, 0, 0);
     }
   };
   u32x4 ka[8], kb[8];
 
-  // query fragment (B operand of S^T): column n = query head kvh*G + n (n < G)
-  bf16x8 qf[8];
-  {
-    const bool col_ok = n < a.grp;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.hq + kvh * a.grp + (col_ok ? n : 0)) * kD;
-    u32x4 raw[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      raw[kk] = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
-    if (remote) {
-      const int p = a.n_kv - 1;
-      const long long cq = (long long)(p / a.g) - p;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u32x4 lo, hi;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          float y1[2], y2[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int e = 2 * e2 + t;
-            const f32x2 cs = rot_cs(cq, a.theta_rev[16 * kk + 8 * h + e]);
-            const float x1 = elem(raw[kk], e), x2 = elem(raw[kk + 4], e);
-            y1[t] = x1 * cs.x - x2 * cs.y;
-            y2[t] = x2 * cs.x + x1 * cs.y;
-          }
-          lo[e2] = pack_bf16(y1[0], y1[1]);
-          hi[e2] = pack_bf16(y2[0], y2[1]);
-        }
-        raw[kk] = lo;
-        raw[kk + 4] = hi;
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(raw[kk]);
+  // Loads in the order they are needed: this lane's angle-table entries and
+  // query fragment first (tiny), then the first two key/value blocks, so that
+  // waiting for the former never waits for the stream.
+  double th64 = 0.0;
+  float th32 = 0.0f;
+  if (BIF) {  // unconditional within the instantiation: keeps the wait for them exact
+    th64 = a.theta_rev[lane];
+    th32 = a.theta_rev32[lane];
   }
-
-  // Remote keys: c(j) = c(ws) - u(j), u = t - floor((r + t)/g), t = j - ws,
-  // r = ws mod g.  The angle c(ws) theta_d is reduced in fp64 once per wave;
-  // the small per-key part u theta_d (u < 128) is exact enough in fp32.
-  int r_s = 0;
-  if (BIF && remote) {
-    const long long cb = (long long)(ws / a.g) - ws;
-    r_s = ws % a.g;
-    const double r = (double)cb * a.theta_rev[lane];
-    s_fb[wave][lane] = (float)(r - __builtin_rint(r));
-    s_th[wave][lane] = a.theta_rev32[lane];
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // first two blocks in flight (after the query and table loads above, whose
-  // completion the loop then never has to wait for)
+  const bool col_ok = n < a.grp;
+  const uint16_t* qrow = a.q + ((int64_t)b * a.hq + kvh * a.grp + (col_ok ? n : 0)) * kD;
+  u32x4 qraw[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    qraw[kk] = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
   issue(0, ka, 0);
   issue(1, kb, 1);
+  // Everything below reads data loaded above; waiting for block 0 (and so for
+  // the older table and query loads) explicitly keeps the wait exact.
+  wait_vmem_at_most<kVmemPerBlock>();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // query fragment (B operand of S^T): column n = query head kvh*G + n (n < G),
+  // as stored; its correction is folded into the keys' angle below
+  bf16x8 qf[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(qraw[kk]);
+
+  // Remote keys.  Rotations in the same planes commute and are orthogonal, so
+  // the grouped score rot(q, c(p) theta) . rot(k_j, c(j) theta) equals
+  // q . rot(k_j, (c(j) - c(p)) theta): only the key turns, by
+  //   (c(j) - c(p)) theta_d = (c(ws) - c(p)) theta_d - u(j) theta_d,
+  //   u = t - floor((r + t)/g), t = j - ws, r = ws mod g.
+  // The wave's part is reduced in fp64 once; the per-key part u theta_d
+  // (u < 512) is exact enough in fp32, and the sum (below 82 revolutions) lies
+  // inside the domain of the hardware sine and cosine, which reduce it exactly.
+  int r_s = 0;
+  if (BIF && remote) {
+    const int p = a.n_kv - 1;
+    const long long cb = ((long long)(ws / a.g) - ws) - ((long long)(p / a.g) - p);
+    r_s = ws % a.g;
+    const double r = (double)cb * th64;
+    s_fb[wave][lane] = (float)(r - __builtin_rint(r));
+    s_th[wave][lane] = th32;
+    __builtin_amdgcn_wave_barrier();
+  }
 
   // lane-constant part of the transposed V reads (see the prefill kernel)
   const int jl = lane & 15;
@@ -199,6 +212,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     // block blk's loads are older than the (up to) 16 of block blk+1
     if (more) wait_vmem_at_most<kVmemPerBlock>();
     else wait_vmem_at_most<0>();
+    __builtin_amdgcn_sched_barrier(0);  // nothing that reads the block may move above the wait
     if (BIF && remote) {
       const int t = j0 + perm_key(n) - ws;
       const float uf = (float)(t - small_div(r_s + t, a.g, a.inv_g));
@@ -277,24 +291,28 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
     }
   };
 
-  // Fully unrolled over the 4 blocks of a wave, with every load issued
-  // unconditionally (blocks past the end of the wave's range re-read its last
-  // key and are masked out entirely), so that the waits on the prefetched
-  // block are exact.
-  static_assert(kKeysPerWave == 4 * kBlk, "four blocks per wave");
-  process(0, ka, 0, true);
-  __builtin_amdgcn_wave_barrier();  // the V buffer is free again once its reads returned
-  issue(2, ka, 0);
-  process(1, kb, 1, true);
-  __builtin_amdgcn_wave_barrier();
-  issue(3, kb, 1);
-  process(2, ka, 0, true);
-  process(3, kb, 1, false);
+  // Blocks in pairs (the two register/LDS buffers alternate), every load
+  // issued unconditionally (blocks past the end of the wave's range re-read
+  // its last key and are masked out entirely), so that the wait on the
+  // prefetched block is exact: only block b+1's loads are newer than block b's.
+  static_assert(kKeysPerWave % (2 * kBlk) == 0 && kKeysPerWave >= 4 * kBlk, "whole block pairs per wave");
+  constexpr int kBlocks = kKeysPerWave / kBlk;
+#pragma unroll 1
+  for (int blk = 0; blk < kBlocks - 2; blk += 2) {
+    process(blk, ka, 0, true);
+    __builtin_amdgcn_wave_barrier();  // the V buffer is free again once its reads returned
+    issue(blk + 2, ka, 0);
+    process(blk + 1, kb, 1, true);
+    __builtin_amdgcn_wave_barrier();
+    issue(blk + 3, kb, 1);
+  }
+  process(kBlocks - 2, ka, 0, true);
+  process(kBlocks - 1, kb, 1, false);
 
-  // ---- merge the four waves' partial softmaxes of this chunk ----
+  // ---- merge the waves' partial softmaxes of this chunk ----
   const float lt = half_sum(l_run);
   __syncthreads();  // every wave is done with its V buffers
-  float* red = reinterpret_cast<float*>(&s_v0[0][0]);  // [wave][G][D] fp32 (32 KB)
+  float* red = reinterpret_cast<float*>(&s_v0[0][0]);  // [wave][G][D] fp32, at most the 16 KiB of s_v0
   if (n < a.grp) {
     if (h == 0) {
       s_m[wave][n] = m_run * a.scale_log2;  // log2 units
@@ -330,53 +348,80 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_split_kernel(const Deco
 }
 
 // Merge the per-chunk partials of one (sequence, query head): lse-weighted sum.
-// 256 threads: 8 groups of 32 threads; a group walks every 8th chunk, each of
-// its threads owning 4 of the 128 output columns (one 512-byte row per step).
+// 256 threads = 8 chunk lanes x 32 threads, each thread owning 4 of the 128
+// output columns.  A chunk lane takes every 8th partial; all of a round's loads
+// (up to 16 partials per thread) are issued together and merged with a running
+// maximum, so a whole head costs one memory round trip per 128 partials.  The
+// 8 lanes are then merged through LDS.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineLanes = kCombineThreads / 32;
+constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* part_o, const float* part_lse,
                                                                          uint16_t* out, float* lse, int n_wg) {
-  __shared__ float s_red[kCombineThreads / 64];
-  __shared__ float4 s_acc[8][32];
-  __shared__ float s_w[8];
+  __shared__ float4 s_o[kCombineLanes][32];
+  __shared__ float s_m[kCombineLanes];
+  __shared__ float s_l[kCombineLanes];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
+  const int cl = tid >> 5, c4 = tid & 31;
   const float* pl = part_lse + bh * n_wg;
-  // maximum over chunks
-  float mx = -INFINITY;
-  for (int s = tid; s < n_wg; s += kCombineThreads) mx = fmaxf(mx, pl[s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  // weighted sum
-  const int grp = tid >> 5, c4 = tid & 31;
+  const float* po = part_o + bh * n_wg * kD + 4 * c4;
+  float m = -INFINITY, l = 0.0f;
   float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-  float wsum = 0.0f;
-#pragma unroll 4
-  for (int s = grp; s < n_wg; s += 8) {
-    const float w = __expf(pl[s] - mx);
-    const float4 x = *reinterpret_cast<const float4*>(part_o + (bh * n_wg + s) * kD + 4 * c4);
-    o.x += w * x.x;
-    o.y += w * x.y;
-    o.z += w * x.z;
-    o.w += w * x.w;
-    wsum += w;
+  for (int s0 = cl; s0 < n_wg; s0 += kCombineLanes * kCombineBatch) {
+    float lv[kCombineBatch];
+    float4 x[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int s = s0 + kCombineLanes * i;
+      const bool ok = s < n_wg;
+      lv[i] = ok ? pl[s] : -INFINITY;
+      x[i] = ok ? *reinterpret_cast<const float4*>(po + (int64_t)s * kD) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // lv[0] belongs to partial s0 < n_wg, whose chunk is non-empty: mx is finite
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) mx = fmaxf(mx, lv[i]);
+    const float sc = __expf(m - mx);  // 0 on the first round (m = -inf)
+    l *= sc;
+    o.x *= sc;
+    o.y *= sc;
+    o.z *= sc;
+    o.w *= sc;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const float w = __expf(lv[i] - mx);  // 0 for the padding entries
+      l += w;
+      o.x += w * x[i].x;
+      o.y += w * x[i].y;
+      o.z += w * x[i].z;
+      o.w += w * x[i].w;
+    }
+    m = mx;
   }
-  s_acc[grp][c4] = o;
-  if (c4 == 0) s_w[grp] = wsum;
+  s_o[cl][c4] = o;
+  if (c4 == 0) {
+    s_m[cl] = m;
+    s_l[cl] = l;
+  }
   __syncthreads();
   if (tid < 32) {
-    float4 t = s_acc[0][tid];
-    float ws = s_w[0];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int gi = 1; gi < 8; ++gi) {
-      const float4 x = s_acc[gi][tid];
-      t.x += x.x;
-      t.y += x.y;
-      t.z += x.z;
-      t.w += x.w;
-      ws += s_w[gi];
+    for (int g = 0; g < kCombineLanes; ++g)
+      if (s_l[g] > 0.0f) mx = fmaxf(mx, s_m[g]);
+    float ws = 0.0f;
+    float4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < kCombineLanes; ++g) {
+      if (!(s_l[g] > 0.0f)) continue;  // a lane with no partials (n_wg < 8)
+      const float sc = __expf(s_m[g] - mx);
+      const float4 x = s_o[g][tid];
+      ws += s_l[g] * sc;
+      t.x += x.x * sc;
+      t.y += x.y * sc;
+      t.z += x.z * sc;
+      t.w += x.w * sc;
     }
     const float inv = 1.0f / ws;
     const u32x2 pk = {pack_bf16(t.x * inv, t.y * inv), pack_bf16(t.z * inv, t.w * inv)};
