@@ -14,10 +14,11 @@ head_dim 128, seq 131072, pretrained window 32768, local window 4096, RoPE base
 
 Printed (one JSON line): prefill TFLOP/s on the algorithmic count
 4*D*Hq*B*s(s+1)/2 as ``value``; the roofline of the prefill kernel (bf16 MFMA
-peak 2.5 PFLOP/s); decode HBM GB/s over the K+V bytes (caches rotated so the
-256 MB last-level cache cannot hold them) and its overhead vs the plain decode
-built the same way; the plain causal prefill for comparison; and the fp64 CPU
-oracle timed on a bounded sample of rows.
+peak 2.5 PFLOP/s); decode HBM GB/s over the K+V bytes at caches of 32K, 64K
+and 128K positions (cache slices rotated so the 256 MB last-level cache cannot
+hold them) and its overhead vs the plain decode built the same way; the plain
+causal prefill for comparison; and the fp64 CPU oracle timed on a bounded sample
+of rows.
 """
 
 from __future__ import annotations
@@ -37,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "bifocal prefill TFLOP/s @128K (% MFMA peak) + decode GB/s and overhead vs plain"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+DECODE_LENGTHS = (32768, 65536, 131072)
 
 WORKLOADS = {
     # name: (workload id, batch, seq, Hq, Hkv, L, W, base)
@@ -117,7 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3_8b_128k", choices=sorted(WORKLOADS))
-    ap.add_argument("--decode-iters", type=int, default=60)
+    ap.add_argument("--decode-iters", type=int, default=200, help="timed decode calls per mode and length")
+    ap.add_argument("--decode-warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the plain-prefill and decode comparisons")
@@ -250,39 +253,59 @@ def main():
         log(f"plain prefill {plain_ms:.2f} ms")
         del out_p
 
-        # decode: rotate among 3 caches (>= 1.5 GB at 128K) so the last-level cache cannot serve them;
-        # bifocal and plain interleaved.
-        caches = [(k, v)]
-        for r in range(2):
-            caches.append((k.clone(), v.clone()))
-        kv_bytes = 2 * b * s * hkv * 128 * 2
-        per = {"bifocal": [], "plain": []}
-        for it in range(args.decode_iters + 5):
-            for mode in ("bifocal", "plain"):
-                kc, vc = caches[it % len(caches)]
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                if mode == "bifocal":
-                    jl.jl_bifocal_decode(q_dec, kc, vc, out_dec, None, big_l, w, base, ws)
-                else:
-                    jl.jl_plain_decode(q_dec, kc, vc, out_dec, None, ws)
-                e1.record(stream)
-                if it >= 5:
-                    per[mode].append((e0, e1))
+        # decode: one query against caches of 32K, 64K and 128K positions (those up to the workload's
+        # length).  Each length rotates among distinct cache slices, 1.5 GiB in total, so that the
+        # 256 MB last-level cache cannot serve them; bifocal and plain interleaved in one process.
+        caches = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+        # A decode call is shorter than the Python launch path at 32K, so calls are queued in batches
+        # behind a short spin kernel: the GPU then runs them back to back and each event pair times
+        # the call on the GPU, not the host's launch overhead.
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        torch.cuda._sleep(1_000_000)
+        e_b.record(stream)
         torch.cuda.synchronize()
-        dec = {}
-        for mode, lst in per.items():
-            us = np.array([a.elapsed_time(bb) * 1e3 for a, bb in lst])
-            dec[mode] = {"us_median": round(float(np.median(us)), 2), "us_min": round(float(us.min()), 2),
-                         "GB_s": round(kv_bytes / (np.median(us) * 1e-6) / 1e9, 1)}
-        dec["kv_bytes"] = kv_bytes
-        dec["hbm_frac"] = round(dec["bifocal"]["GB_s"] / PEAK_HBM_GBS, 4)
-        dec["overhead_vs_plain"] = round(dec["bifocal"]["us_median"] / dec["plain"]["us_median"] - 1.0, 4)
-        dec["g"] = g
-        result["decode"] = dec
-        log(f"decode bifocal {dec['bifocal']['us_median']} us ({dec['bifocal']['GB_s']} GB/s), "
-            f"plain {dec['plain']['us_median']} us, overhead {dec['overhead_vs_plain'] * 100:.2f}%")
-        del caches
+        spin_cycles = int(1_000_000 * 3.0 / max(e_a.elapsed_time(e_b), 1e-3))  # about 3 ms per batch
+        batch_iters = 10
+        sweep = []
+        for n in [x for x in DECODE_LENGTHS if x <= s]:
+            offsets = range(0, s - n + 1, n) if b == 1 else [0]  # a slice along the length is contiguous at B=1
+            slices = [(kc[:, o:o + n], vc[:, o:o + n]) for kc, vc in caches for o in offsets]
+            g_n = jl.jl_group_factor(n, big_l)
+            kv_bytes = 2 * b * n * hkv * 128 * 2
+            per = {"bifocal": [], "plain": []}
+            for it in range(args.decode_warmup + args.decode_iters):
+                if it % batch_iters == 0:
+                    torch.cuda._sleep(spin_cycles)
+                for mi, mode in enumerate(("bifocal", "plain")):
+                    # consecutive calls never share a slice, so neither finds the other's data cached
+                    kc, vc = slices[(2 * it + mi) % len(slices)]
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if mode == "bifocal":
+                        jl.jl_bifocal_decode(q_dec, kc, vc, out_dec, None, big_l, w, base, ws)
+                    else:
+                        jl.jl_plain_decode(q_dec, kc, vc, out_dec, None, ws)
+                    e1.record(stream)
+                    if it >= args.decode_warmup:
+                        per[mode].append((e0, e1))
+            torch.cuda.synchronize()
+            dec = {"n_kv": n, "g": g_n, "kv_bytes": kv_bytes, "timed_runs": args.decode_iters,
+                   "cache_slices": len(slices),
+                   "timing": "HIP events per call on the GPU, calls queued back to back behind a spin kernel"}
+            for mode, lst in per.items():
+                us = np.array([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in lst])
+                dec[mode] = {"us_median": round(float(np.median(us)), 2), "us_min": round(float(us.min()), 2),
+                             "GB_s": round(kv_bytes / (np.median(us) * 1e-6) / 1e9, 1)}
+            dec["hbm_frac"] = round(dec["bifocal"]["GB_s"] / PEAK_HBM_GBS, 4)
+            dec["overhead_vs_plain"] = round(dec["bifocal"]["us_median"] / dec["plain"]["us_median"] - 1.0, 4)
+            sweep.append(dec)
+            log(f"decode n_kv={n} g={g_n}: bifocal {dec['bifocal']['us_median']} us ({dec['bifocal']['GB_s']} GB/s), "
+                f"plain {dec['plain']['us_median']} us, overhead {dec['overhead_vs_plain'] * 100:.2f}%")
+        if sweep and sweep[-1]["n_kv"] == s:
+            result["decode"] = dict(sweep[-1])  # the workload's own length
+        result["decode_sweep"] = sweep
+        del caches, slices
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -214,7 +214,7 @@ jl_status jl_bifocal_prefill_ws(const void* q, const void* k, const void* v, voi
 size_t jl_bifocal_decode_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
                                         int32_t head_dim) {
   if (batch < 1 || n_kv < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim != 128) return 0;
-  return jl::decode_workspace_bytes(batch, n_kv, n_q_heads);
+  return jl::decode_workspace_bytes(batch, n_kv, n_q_heads, n_kv_heads);
 }
 
 static jl_status decode_common(const void* q, const void* k, const void* v, void* out, float* lse, const Shape& s,
@@ -229,7 +229,7 @@ static jl_status decode_common(const void* q, const void* k, const void* v, void
     return fail(JL_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", s.hq / s.hkv);
   JL_TRY(check_scale(scale_in, scale));
   JL_TRY(check_pointer(workspace, "workspace"));
-  const size_t need = jl::decode_workspace_bytes(s.batch, s.n_kv, s.hq);
+  const size_t need = jl::decode_workspace_bytes(s.batch, s.n_kv, s.hq, s.hkv);
   if (workspace_bytes < need)
     return fail(JL_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
                 need);

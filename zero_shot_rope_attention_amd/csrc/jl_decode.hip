@@ -12,8 +12,9 @@
 // (normalised output, log-sum-exp) and a second kernel merges the partials.
 //
 // Per workgroup: one KV head, its G query heads, one chunk of up to 1024 keys
-// (2 waves x 512 keys, each wave streaming its keys in 32-key blocks with the
-// next block in flight).  Two-wave workgroups, four per CU, keep the merge at
+// (2 waves x up to 512 keys, each wave streaming its keys in 32-key blocks with
+// the next block in flight; shorter caches use shorter waves so that about one
+// full round of workgroups remains).  Two-wave workgroups, four per CU, keep the merge at
 // the end of one workgroup from idling a large share of the CU's loads.
 // Per wave and block:
 //   S^T = K Q^T   (MFMA; A = key fragments loaded straight from HBM, 16-byte
@@ -29,9 +30,10 @@
 namespace jl {
 namespace {
 
-constexpr int kKeysPerWave = 512;
 constexpr int kWaves = 2;
-constexpr int kKeysPerWG = kKeysPerWave * kWaves;
+constexpr int kMaxBlocksPerWave = 16;  // 512 keys per wave at most
+// Enough workgroups for one full round at four per CU on 256 CUs.
+constexpr int64_t kTargetWorkgroups = 1024;
 constexpr int kMaxGroup = 16;  // query heads per KV head handled by one workgroup
 
 struct DecodeArgs {
@@ -47,6 +49,8 @@ struct DecodeArgs {
   int32_t remote_end;  // keys [0, remote_end) are remote (grouped scores)
   int32_t n_rem_wg;    // chunks covering the remote prefix
   int32_t n_wg;        // total chunks
+  int32_t nb;          // 32-key blocks per wave (even, 2..16)
+  int32_t kpw;         // keys per wave = 32 nb; a chunk is kWaves * kpw keys
   float inv_g;
   float scale_log2;
   float theta_rev32[kHalfD];
@@ -99,16 +103,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   int ks, ke;
   bool remote = false;
+  const int kpg = kWaves * a.kpw;
   if (sp < a.n_rem_wg) {
-    ks = sp * kKeysPerWG;
-    ke = min(a.remote_end, ks + kKeysPerWG);
+    ks = sp * kpg;
+    ke = min(a.remote_end, ks + kpg);
     remote = BIF;
   } else {
-    ks = a.remote_end + (sp - a.n_rem_wg) * kKeysPerWG;
-    ke = min(a.n_kv, ks + kKeysPerWG);
+    ks = a.remote_end + (sp - a.n_rem_wg) * kpg;
+    ke = min(a.n_kv, ks + kpg);
   }
-  const int ws = ks + wave * kKeysPerWave;
-  const int we = min(ke, ws + kKeysPerWave);
+  const int ws = ks + wave * a.kpw;
+  const int we = min(ke, ws + a.kpw);
 
   const int64_t kv_rs = (int64_t)a.hkv * kD;
   const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   //   (c(j) - c(p)) theta_d = (c(ws) - c(p)) theta_d - u(j) theta_d,
   //   u = t - floor((r + t)/g), t = j - ws, r = ws mod g.
   // The wave's part is reduced in fp64 once; the per-key part u theta_d
-  // (u < 512) is exact enough in fp32, and the sum (below 82 revolutions) lies
+  // (u < 512, the longest wave) is exact enough in fp32, and the sum (below 82 revolutions) lies
   // inside the domain of the hardware sine and cosine, which reduce it exactly.
   int r_s = 0;
   if (BIF && remote) {
@@ -295,10 +300,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // issued unconditionally (blocks past the end of the wave's range re-read
   // its last key and are masked out entirely), so that the wait on the
   // prefetched block is exact: only block b+1's loads are newer than block b's.
-  static_assert(kKeysPerWave % (2 * kBlk) == 0 && kKeysPerWave >= 4 * kBlk, "whole block pairs per wave");
-  constexpr int kBlocks = kKeysPerWave / kBlk;
+  const int n_blocks = a.nb;  // even and >= 2
 #pragma unroll 1
-  for (int blk = 0; blk < kBlocks - 2; blk += 2) {
+  for (int blk = 0; blk < n_blocks - 2; blk += 2) {
     process(blk, ka, 0, true);
     __builtin_amdgcn_wave_barrier();  // the V buffer is free again once its reads returned
     issue(blk + 2, ka, 0);
@@ -306,8 +310,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     __builtin_amdgcn_wave_barrier();
     issue(blk + 3, kb, 1);
   }
-  process(kBlocks - 2, ka, 0, true);
-  process(kBlocks - 1, kb, 1, false);
+  process(n_blocks - 2, ka, 0, true);
+  process(n_blocks - 1, kb, 1, false);
 
   // ---- merge the waves' partial softmaxes of this chunk ----
   const float lt = half_sum(l_run);
@@ -432,10 +436,25 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
 
 }  // namespace
 
-int32_t decode_max_splits(int32_t n_kv) { return (n_kv + kKeysPerWG - 1) / kKeysPerWG + 1; }
+// Blocks per wave: the longest waves (fewest partials) that still give about
+// one full round of workgroups; shorter caches get shorter waves.
+int32_t decode_blocks_per_wave(int32_t batch, int32_t n_kv, int32_t n_kv_heads) {
+  int32_t nb = kMaxBlocksPerWave;
+  while (nb > 2) {
+    const int64_t chunk = (int64_t)kWaves * kBlk * nb;
+    if ((int64_t)batch * n_kv_heads * ((n_kv + chunk - 1) / chunk) >= kTargetWorkgroups) break;
+    nb -= 2;
+  }
+  return nb;
+}
 
-size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads) {
-  const size_t rows = (size_t)batch * n_q_heads * decode_max_splits(n_kv);
+int32_t decode_max_splits(int32_t batch, int32_t n_kv, int32_t n_kv_heads) {
+  const int32_t chunk = kWaves * kBlk * decode_blocks_per_wave(batch, n_kv, n_kv_heads);
+  return (n_kv + chunk - 1) / chunk + 1;
+}
+
+size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads) {
+  const size_t rows = (size_t)batch * n_q_heads * decode_max_splits(batch, n_kv, n_kv_heads);
   return rows * kD * sizeof(float) + rows * sizeof(float);
 }
 
@@ -455,16 +474,26 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   a.g = bifocal ? p.group : 1;
   a.remote_end = bifocal ? p.n_kv - p.local_window : 0;
   if (a.remote_end < 0) a.remote_end = 0;
-  a.n_rem_wg = (a.remote_end + kKeysPerWG - 1) / kKeysPerWG;
-  a.n_wg = a.n_rem_wg + (p.n_kv - a.remote_end + kKeysPerWG - 1) / kKeysPerWG;
+  a.nb = decode_blocks_per_wave(p.batch, p.n_kv, p.n_kv_heads);
+  a.kpw = kBlk * a.nb;
+  const int32_t chunk = kWaves * a.kpw;
+  a.n_rem_wg = (a.remote_end + chunk - 1) / chunk;
+  a.n_wg = a.n_rem_wg + (p.n_kv - a.remote_end + chunk - 1) / chunk;
   a.inv_g = 1.0f / (float)a.g;
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
-  const double two_pi = 6.283185307179586476925286766559;
-  for (int d = 0; d < kHalfD; ++d) {
-    a.theta_rev[d] = std::pow(p.rope_base, -2.0 * d / kD) / two_pi;
-    a.theta_rev32[d] = (float)a.theta_rev[d];
+  // theta_d / (2 pi) for this RoPE base, kept per thread for the next call
+  thread_local double cached_base = 0.0;
+  thread_local double cached_rev[kHalfD];
+  if (cached_base != p.rope_base) {
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int d = 0; d < kHalfD; ++d) cached_rev[d] = std::pow(p.rope_base, -2.0 * d / kD) / two_pi;
+    cached_base = p.rope_base;
   }
-  const size_t rows = (size_t)p.batch * p.n_q_heads * decode_max_splits(p.n_kv);
+  for (int d = 0; d < kHalfD; ++d) {
+    a.theta_rev[d] = cached_rev[d];
+    a.theta_rev32[d] = (float)cached_rev[d];
+  }
+  const size_t rows = (size_t)p.batch * p.n_q_heads * decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);
   a.part_o = static_cast<float*>(p.workspace);
   a.part_lse = a.part_o + rows * kD;
   // partials are laid out with the actual chunk count as the row stride

@@ -47,8 +47,8 @@ struct DecodeProblem {
 
 // Number of key chunks the decode splits a cache of n_kv keys into (upper bound
 // over every local window), and the workspace bytes that many chunks need.
-int32_t decode_max_splits(int32_t n_kv);
-size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads);
+int32_t decode_max_splits(int32_t batch, int32_t n_kv, int32_t n_kv_heads);
+size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads);
 
 hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t stream);
 
