@@ -129,17 +129,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // load, never for the older ones alone.
   const uint32_t row_bytes = (uint32_t)kv_rs * 2u;  // <= 16 MiB (n_kv_heads <= 65536)
   typedef __attribute__((address_space(3))) void lds_void;
-  auto issue = [&](int blk, u32x4 (&kr)[8], int buf) {
+  auto rsrc_for = [&](const uint16_t* base, int jb, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
+  };
+  auto issue_k = [&](int blk, u32x4 (&kr)[8]) {
     const int j0 = ws + blk * kBlk;
     const int jb = min(j0, we - 1);
     const uint32_t nbytes = (uint32_t)min(kBlk, we - jb) * row_bytes;
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t krs = rsrc_for(kbase, jb, nbytes);
     const uint32_t ko = (uint32_t)(min(j0 + perm_key(n), we - 1) - jb) * row_bytes + 16u * (uint32_t)h;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) kr[kk] = __builtin_amdgcn_raw_buffer_load_b128(krs, ko + 32u * kk, 0, 0);
+  };
+  auto issue_v = [&](int blk, int buf) {
+    const int j0 = ws + blk * kBlk;
+    const int jb = min(j0, we - 1);
+    const uint32_t nbytes = (uint32_t)min(kBlk, we - jb) * row_bytes;
+    const __amdgpu_buffer_rsrc_t vrs = rsrc_for(vbase, jb, nbytes);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 4 * r + (lane >> 4);
@@ -148,6 +154,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(buf ? &s_v1[wave][r * 1024] : &s_v0[wave][r * 1024]),
                                                16, (int)vo, 0, 0, 0);
     }
+  };
+  auto issue = [&](int blk, u32x4 (&kr)[8], int buf) {
+    issue_k(blk, kr);
+    issue_v(blk, buf);
   };
   u32x4 ka[8], kb[8];
 
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x16{};
 
-  auto process = [&](int blk, u32x4 (&kr)[8], int buf, bool more) {
+  auto process = [&](int blk, u32x4 (&kr)[8], int buf, bool more, int next_blk) {
     const int j0 = ws + blk * kBlk;
     // block blk's loads are older than the (up to) 16 of block blk+1
     if (more) wait_vmem_at_most<kVmemPerBlock>();
@@ -253,6 +263,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     f32x16 s = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = mfma32(as_bf16x8(kr[kk]), qf[kk], s);
+    // Bifocal: the key registers are free once S is formed, so the next key
+    // fragment is requested before the softmax rather than after the block (the
+    // rotation lengthens every block).  Plain keeps both requests after the block.
+    if (BIF && next_blk >= 0) issue_k(next_blk, kr);
 
     // online softmax (lazy rescale, as in the prefill): lane = head n, keys j0 + 16h + i
     float mloc = -INFINITY;
@@ -299,19 +313,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // Blocks in pairs (the two register/LDS buffers alternate), every load
   // issued unconditionally (blocks past the end of the wave's range re-read
   // its last key and are masked out entirely), so that the wait on the
-  // prefetched block is exact: only block b+1's loads are newer than block b's.
+  // prefetched block is exact: only block b+1's loads are newer than block b's
+  // (block b+2's are issued after that wait).
   const int n_blocks = a.nb;  // even and >= 2
 #pragma unroll 1
   for (int blk = 0; blk < n_blocks - 2; blk += 2) {
-    process(blk, ka, 0, true);
+    process(blk, ka, 0, true, blk + 2);
     __builtin_amdgcn_wave_barrier();  // the V buffer is free again once its reads returned
-    issue(blk + 2, ka, 0);
-    process(blk + 1, kb, 1, true);
+    if (!BIF) issue_k(blk + 2, ka);
+    issue_v(blk + 2, 0);
+    process(blk + 1, kb, 1, true, blk + 3);
     __builtin_amdgcn_wave_barrier();
-    issue(blk + 3, kb, 1);
+    if (!BIF) issue_k(blk + 3, kb);
+    issue_v(blk + 3, 1);
   }
-  process(n_blocks - 2, ka, 0, true);
-  process(n_blocks - 1, kb, 1, false);
+  process(n_blocks - 2, ka, 0, true, -1);
+  process(n_blocks - 1, kb, 1, false, -1);
 
   // ---- merge the waves' partial softmaxes of this chunk ----
   const float lt = half_sum(l_run);
