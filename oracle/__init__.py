@@ -38,5 +38,7 @@ from .bifocal import (  # noqa: F401
     bifocal_three_pass,
     bifocal_bruteforce,
     bifocal_decode,
+    bifocal_decode_varlen,
+    plain_decode_varlen,
     merge_passes,
 )

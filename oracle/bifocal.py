@@ -29,6 +29,10 @@ Parity pins (see ``tests/test_oracle_*.py``):
 * ``plain_causal_attention``: torch fp64 ``scaled_dot_product_attention``.
 * ``bifocal_decode``: it is ``bifocal_three_pass`` at one query row, pinned by the
   same tests plus the decode-equals-last-prefill-row check.
+* ``bifocal_decode_varlen`` / ``plain_decode_varlen``: each sequence equals
+  ``bifocal_bruteforce`` (per-pair position selection, g from that sequence's own
+  length) on its own prefix, with the cache rows past the prefix set to NaN; with
+  every length <= L the two functions agree (exact recovery of the base model).
 
 Where the pages are silent the reading taken is the plainest one the rest
 supports; each is named where it is used.
@@ -52,6 +56,8 @@ __all__ = [
     "bifocal_three_pass",
     "bifocal_bruteforce",
     "bifocal_decode",
+    "bifocal_decode_varlen",
+    "plain_decode_varlen",
     "merge_passes",
 ]
 
@@ -422,3 +428,37 @@ def bifocal_decode(q, k_cache, v_cache, pretrained_window, local_window, rope_ba
     r = bifocal_three_pass(q, k_cache, v_cache, pretrained_window, local_window, rope_base,
                            softmax_scale=softmax_scale)
     return r["out"], r["lse"]
+
+
+def bifocal_decode_varlen(q, k_cache, v_cache, seq_lens, pretrained_window, local_window, rope_base,
+                          softmax_scale=None):
+    """A batch of sequences of different lengths, one new token each.  Sequence
+    b holds the first ``seq_lens[b]`` rows of its cache at their original
+    positions and its query sits at ``seq_lens[b] - 1``; the long-range factor
+    is taken from that sequence's own length (seventnews.com, "How bifocal
+    attention sidesteps the fixed-scaling trap": the factor follows the current
+    length).  Each sequence is exactly the decode above on its own prefix.
+    ``q`` is ``[B, 1, Hq, D]``, caches ``[B, N, Hkv, D]`` with N >= max(seq_lens).
+    Returns ``(out [B, 1, Hq, D], lse [B, Hq, 1])``.
+    """
+    q = _as_f64(q)
+    outs, lses = [], []
+    for bi, s in enumerate(int(x) for x in seq_lens):
+        o, l = bifocal_decode(q[bi:bi + 1], k_cache[bi:bi + 1, :s], v_cache[bi:bi + 1, :s], pretrained_window,
+                              local_window, rope_base, softmax_scale=softmax_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs, axis=0), np.concatenate(lses, axis=0)
+
+
+def plain_decode_varlen(q, k_cache, v_cache, seq_lens, softmax_scale=None):
+    """The base model's decode for a batch of sequences of different lengths:
+    plain causal attention of the query at ``seq_lens[b] - 1`` over its own prefix."""
+    q = _as_f64(q)
+    outs, lses = [], []
+    for bi, s in enumerate(int(x) for x in seq_lens):
+        o, l = plain_causal_attention(q[bi:bi + 1], k_cache[bi:bi + 1, :s], v_cache[bi:bi + 1, :s],
+                                      softmax_scale=softmax_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs, axis=0), np.concatenate(lses, axis=0)

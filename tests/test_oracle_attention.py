@@ -240,3 +240,41 @@ def test_parity_bar_detects_seam_shift():
     right, _ = oracle.bifocal_bruteforce(q_raw * 2, k_raw, v, big_l, w, 1e4)
     wrong, _ = oracle.bifocal_bruteforce(q_raw * 2, k_raw, v, big_l, w, 1e4, select=shifted)
     assert _fails_bar(wrong, right, 5)
+
+
+def test_decode_varlen_equals_bruteforce_per_sequence():
+    # three sequences in one padded cache: lengths 5, 17, 40 with L = 8, W = 3 give
+    # g = 1, 3, 5, i.e. plain, bifocal, and bifocal with a larger factor; rows past a
+    # sequence's length are NaN, so a read beyond its prefix would poison its output
+    big_l, w, base, d, hq, hkv = 8, 3, 1e4, 16, 4, 2
+    lens = [5, 17, 40]
+    n_max = max(lens)
+    rng = np.random.default_rng(4242)
+    q = np.zeros((3, 1, hq, d))
+    k = np.full((3, n_max, hkv, d), np.nan)
+    v = np.full((3, n_max, hkv, d), np.nan)
+    expect = []
+    for bi, s in enumerate(lens):
+        q_raw = rng.standard_normal((1, 1, hq, d))
+        k_raw = rng.standard_normal((1, s, hkv, d))
+        v_s = rng.standard_normal((1, s, hkv, d))
+        q_rot, k_rot = _prerotate(q_raw, k_raw, base)
+        q[bi], k[bi, :s], v[bi, :s] = q_rot[0], k_rot[0], v_s[0]
+        expect.append(oracle.bifocal_bruteforce(q_raw, k_raw, v_s, big_l, w, base))
+    out, lse = oracle.bifocal_decode_varlen(q, k, v, lens, big_l, w, base)
+    assert [oracle.group_factor(s, big_l) for s in lens] == [1, 3, 5]
+    for bi in range(3):
+        o2, l2 = expect[bi]
+        assert np.abs(out[bi:bi + 1] - o2).max() <= 1e-12 * np.nanmax(np.abs(v))
+        assert np.abs(lse[bi:bi + 1] - l2).max() <= 1e-11
+    # with every length inside the pretrained window the method is the base model
+    out_b, lse_b = oracle.bifocal_decode_varlen(q, k, v, lens, 64, w, base)
+    out_p, lse_p = oracle.plain_decode_varlen(q, k, v, lens)
+    assert np.abs(out_b - out_p).max() <= 1e-12 and np.abs(lse_b - lse_p).max() <= 1e-12
+    # and plain matches torch's fp64 attention of each query over its own prefix
+    for bi, s in enumerate(lens):
+        qt = torch.from_numpy(q[bi:bi + 1]).permute(0, 2, 1, 3)
+        kt = torch.from_numpy(np.repeat(k[bi:bi + 1, :s], hq // hkv, axis=2)).permute(0, 2, 1, 3)
+        vt = torch.from_numpy(np.repeat(v[bi:bi + 1, :s], hq // hkv, axis=2)).permute(0, 2, 1, 3)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).permute(0, 2, 1, 3).numpy()
+        assert np.abs(out_p[bi:bi + 1] - ref).max() <= 1e-12
