@@ -307,6 +307,49 @@ def main():
         result["decode_sweep"] = sweep
         del caches, slices
 
+        # variable-length batched decode: 8 sequences of 16K..128K keys (g = 1..4 within one
+        # launch) in a padded cache; rate = K+V bytes the sequences hold / time
+        if b == 1 and s >= 131072:
+            lens = [s - i * (s // 8) for i in range(8)]
+            kv_b = torch.empty((8, s, hkv, 128), dtype=torch.bfloat16, device=dev)
+            vv_b = torch.empty_like(kv_b)
+            for i in range(8):
+                kv_b[i].copy_(k[0])
+                vv_b[i].copy_(v[0])
+            q_b = q[:, -8:].reshape(8, 1, hq, 128).contiguous()
+            out_b = torch.empty_like(q_b)
+            sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+            ws_b = torch.empty(jl.jl_bifocal_decode_workspace_size(8, s, hq, hkv), dtype=torch.uint8, device=dev)
+            held = 2 * sum(lens) * hkv * 128 * 2
+            per = {"bifocal": [], "plain": []}
+            for it in range(args.decode_warmup + args.decode_iters // 4):
+                if it % batch_iters == 0:
+                    torch.cuda._sleep(spin_cycles)
+                for mode in ("bifocal", "plain"):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if mode == "bifocal":
+                        jl.jl_bifocal_decode_varlen(q_b, kv_b, vv_b, out_b, None, sl, big_l, w, base, ws_b)
+                    else:
+                        jl.jl_plain_decode_varlen(q_b, kv_b, vv_b, out_b, None, sl, ws_b)
+                    e1.record(stream)
+                    if it >= args.decode_warmup:
+                        per[mode].append((e0, e1))
+            torch.cuda.synchronize()
+            vl = {"seq_lens": lens, "g": [jl.jl_group_factor(x, big_l) for x in lens], "kv_bytes_held": held,
+                  "timed_runs": args.decode_iters // 4,
+                  "timing": "HIP events per call on the GPU, calls queued back to back behind a spin kernel"}
+            for mode, lst in per.items():
+                us = np.array([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in lst])
+                vl[mode] = {"us_median": round(float(np.median(us)), 2), "us_min": round(float(us.min()), 2),
+                            "GB_s": round(held / (np.median(us) * 1e-6) / 1e9, 1)}
+            vl["hbm_frac"] = round(vl["bifocal"]["GB_s"] / PEAK_HBM_GBS, 4)
+            vl["overhead_vs_plain"] = round(vl["bifocal"]["us_median"] / vl["plain"]["us_median"] - 1.0, 4)
+            result["decode_varlen"] = vl
+            log(f"decode varlen 8 x (16K..128K): bifocal {vl['bifocal']['us_median']} us ({vl['bifocal']['GB_s']} GB/s), "
+                f"plain {vl['plain']['us_median']} us, overhead {vl['overhead_vs_plain'] * 100:.2f}%")
+            del kv_b, vv_b
+
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, args.cpu_rows)

@@ -168,6 +168,39 @@ jl_status jl_plain_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bifocal decode of a batch of sequences of different lengths: one new token
+ * per sequence, each against its own cache prefix, with g taken per sequence
+ * (seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap": the
+ * long-range factor follows the current length; ResearchPod transcript, cache
+ * exchange: the cache keeps original positions, so g can change as it grows).
+ *   seq_lens       : device int32 [B], 4-byte aligned, not NULL; sequence b holds
+ *                    s_b = seq_lens[b] keys, 1 <= s_b <= max_seq_len (device contents are not
+ *                    checked on the host; a length outside the range gives an unspecified
+ *                    result but no access outside the cache)
+ *   q              : bf16 [B, 1, Hq, D]; row b rotated at position s_b - 1
+ *   k_cache/v_cache: bf16 [B, max_seq_len, Hkv, D]; sequence b's keys are rows 0 .. s_b-1
+ *                    at their original positions; rows past s_b are never read
+ *   out, lse       : as jl_bifocal_decode
+ *   workspace      : >= jl_bifocal_decode_workspace_size(B, max_seq_len, Hq, Hkv, D) bytes
+ * Sequence b gets what jl_bifocal_decode returns for it alone with n_kv = s_b (a
+ * sequence with g(s_b) == 1 is the plain decode), up to rounding order: the cache
+ * is cut into chunks sized from B, max_seq_len and Hkv.  With every s_b equal to
+ * max_seq_len the result is bitwise that of jl_bifocal_decode on the same batch. */
+jl_status jl_bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                   float* lse, const int32_t* seq_lens, int32_t batch,
+                                   int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int64_t pretrained_window, int64_t local_window,
+                                   double rope_base, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Plain decode of a batch of sequences of different lengths (same layouts and
+ * kernels as jl_bifocal_decode_varlen, no correction). */
+jl_status jl_plain_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                 float* lse, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,6 +128,32 @@ def test_decode_workspace_and_validation(lib):
     assert dec(d=96, wsb=need) == UNSUPPORTED
 
 
+def test_decode_varlen_validation(lib):
+    need = lib.jl_bifocal_decode_workspace_size(3, 100, 4, 2, 128)
+
+    def dec(plain=False, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, lens=FAKE, batch=3, n_max=100, hq=4, hkv=2, d=128,
+                 big_l=32, w=8, base=1e4, scale=0.0, ws=FAKE, wsb=need)
+        a.update(kw)
+        if plain:
+            return lib.jl_plain_decode_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["lens"], a["batch"],
+                                              a["n_max"], a["hq"], a["hkv"], a["d"], a["scale"], a["ws"], a["wsb"],
+                                              None)
+        return lib.jl_bifocal_decode_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["lens"], a["batch"],
+                                            a["n_max"], a["hq"], a["hkv"], a["d"], a["big_l"], a["w"], a["base"],
+                                            a["scale"], a["ws"], a["wsb"], None)
+
+    for plain in (False, True):
+        assert dec(plain, lens=None) == INVALID            # the lengths are required
+        assert dec(plain, lens=FAKE + 2) == INVALID        # int32 alignment
+        assert dec(plain, wsb=need - 1) == WORKSPACE       # sized for max_seq_len
+        assert dec(plain, n_max=0) == INVALID
+        assert dec(plain, d=64) == UNSUPPORTED
+        if not _has_gpu():
+            assert dec(plain) == DEVICE                    # arguments fine, no device here
+    assert dec(w=33) == INVALID                            # W > L
+
+
 def test_prefill_ws_workspace_and_validation(lib):
     # one corrected copy of the keys: B * n_kv * Hkv * 128 bf16
     assert lib.jl_bifocal_prefill_workspace_size(1, 131072, 8, 128) == 131072 * 8 * 128 * 2

@@ -27,6 +27,8 @@ __all__ = [
     "jl_bifocal_decode_workspace_size",
     "jl_bifocal_decode",
     "jl_plain_decode",
+    "jl_bifocal_decode_varlen",
+    "jl_plain_decode_varlen",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
@@ -50,6 +52,10 @@ _SIGNATURES = {
     "jl_bifocal_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64, _f32,
                                  _vp, _sz, _vp]),
     "jl_plain_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "jl_bifocal_decode_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
+                                        _f32, _vp, _sz, _vp]),
+    "jl_plain_decode_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz,
+                                      _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -169,3 +175,35 @@ def jl_plain_decode(q, k_cache, v_cache, out, lse, workspace, softmax_scale=0.0,
     nbytes = workspace.numel() * workspace.element_size()
     _check(load_library().jl_plain_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b, n_kv, hq,
                                           hkv, d, float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def _seq_lens_ptr(seq_lens):
+    import torch
+    if seq_lens is None:
+        return None
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be an int32 device tensor")
+    return _ptr(seq_lens)
+
+
+def jl_bifocal_decode_varlen(q, k_cache, v_cache, out, lse, seq_lens, pretrained_window, local_window, rope_base,
+                             workspace, softmax_scale=0.0, stream=None):
+    """q [B, 1, Hq, D]; caches [B, max_seq_len, Hkv, D]; seq_lens int32 [B] on the
+    device (keys held by each sequence); workspace as for jl_bifocal_decode with
+    n_kv = max_seq_len."""
+    b, _, hq, d = q.shape
+    n_max, hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_decode_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _seq_lens_ptr(seq_lens), b, n_max, hq, hkv, d,
+        int(pretrained_window), int(local_window), float(rope_base), float(softmax_scale), _ptr(workspace), nbytes,
+        _stream(stream)))
+
+
+def jl_plain_decode_varlen(q, k_cache, v_cache, out, lse, seq_lens, workspace, softmax_scale=0.0, stream=None):
+    b, _, hq, d = q.shape
+    n_max, hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_plain_decode_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _seq_lens_ptr(seq_lens), b, n_max, hq, hkv, d,
+        float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))

@@ -243,7 +243,8 @@ jl_status jl_plain_decode(const void* q, const void* k_cache, const void* v_cach
   const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
   JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
   JL_TRY(device_check());
-  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, batch, n_kv, n_q_heads, n_kv_heads, 1, 0, 2.0, scale, workspace};
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, nullptr, batch, n_kv, n_q_heads, n_kv_heads, 1, 0, 2.0, scale,
+                      workspace};
   return launched(jl::launch_decode(false, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -258,9 +259,47 @@ jl_status jl_bifocal_decode(const void* q, const void* k_cache, const void* v_ca
   JL_TRY(device_check());
   const int64_t g = jl_group_factor(n_kv, pretrained_window);
   const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
-  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, batch, n_kv, n_q_heads, n_kv_heads, (int32_t)g, w, rope_base,
-                      scale, workspace};
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, nullptr, batch, n_kv, n_q_heads, n_kv_heads, pretrained_window,
+                      w, rope_base, scale, workspace};
   return launched(jl::launch_decode(g > 1, p, static_cast<hipStream_t>(stream)));
+}
+
+static jl_status check_seq_lens(const int32_t* seq_lens) {
+  if (!seq_lens) return fail(JL_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (reinterpret_cast<uintptr_t>(seq_lens) % 4 != 0) return fail(JL_ERR_INVALID_ARG, "seq_lens is not 4-byte aligned");
+  return JL_OK;
+}
+
+jl_status jl_plain_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, 1, max_seq_len, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  JL_TRY(check_seq_lens(seq_lens));
+  JL_TRY(device_check());
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads, 1, 0, 2.0,
+                      scale, workspace};
+  return launched(jl::launch_decode(false, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                   int64_t local_window, double rope_base, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, 1, max_seq_len, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  JL_TRY(check_seq_lens(seq_lens));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(device_check());
+  // g(s_b) is taken per sequence in the kernels; a sequence with g = 1 is computed as plain attention
+  const int32_t w = (int32_t)(local_window < max_seq_len ? local_window : max_seq_len);
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, seq_lens, batch, max_seq_len, n_q_heads, n_kv_heads,
+                      pretrained_window, w, rope_base, scale, workspace};
+  return launched(jl::launch_decode(true, p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

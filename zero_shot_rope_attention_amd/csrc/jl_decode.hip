@@ -44,18 +44,40 @@ struct DecodeArgs {
   float* lse;
   float* part_o;    // [B, Hq, n_wg, D]
   float* part_lse;  // [B, Hq, n_wg]
-  int32_t batch, n_kv, hq, hkv, grp;
-  int32_t g;
-  int32_t remote_end;  // keys [0, remote_end) are remote (grouped scores)
-  int32_t n_rem_wg;    // chunks covering the remote prefix
-  int32_t n_wg;        // total chunks
+  const int32_t* seq_lens;  // [B] keys held by each sequence, or null: every sequence holds n_kv
+  int32_t batch, n_kv, hq, hkv, grp;  // n_kv: cache positions per sequence (the cache's stride)
+  int64_t pretrained_window;          // L
+  int32_t local_window;               // W (clamped to each sequence's length)
+  int32_t n_wg;        // chunk slots per sequence (grid x; the partials' row stride)
   int32_t nb;          // 32-key blocks per wave (even, 2..16)
   int32_t kpw;         // keys per wave = 32 nb; a chunk is kWaves * kpw keys
-  float inv_g;
   float scale_log2;
   float theta_rev32[kHalfD];
   double theta_rev[kHalfD];
 };
+
+// How one sequence of s keys is cut: g = g(s) for the bifocal kernel (1 for
+// plain); with g > 1 the remote prefix [0, s - min(W, s)) is cut into n_rem
+// chunks of kpg keys and the local suffix into the rest, so that no chunk
+// straddles the boundary; with g = 1 every chunk is local (base scores).
+struct SeqSplit {
+  int g, remote_end, n_rem, n_chunks;
+};
+__device__ __forceinline__ SeqSplit seq_split(int s, bool bif, int64_t big_l, int w_req, int kpg) {
+  SeqSplit r;
+  r.g = bif ? (int)((int64_t)(s - 1) / big_l + 1) : 1;  // smallest g with floor((s-1)/g) <= L-1
+  const int w = min(w_req, s);
+  r.remote_end = r.g > 1 ? s - w : 0;
+  r.n_rem = (r.remote_end + kpg - 1) / kpg;
+  r.n_chunks = r.n_rem + (s - r.remote_end + kpg - 1) / kpg;
+  return r;
+}
+
+// Keys of sequence b: seq_lens[b] clamped into [1, n_kv] (a length outside the
+// contract gives an unspecified result, never an access outside the cache).
+__device__ __forceinline__ int seq_length(const int32_t* seq_lens, int b, int n_kv) {
+  return seq_lens ? min(max(seq_lens[b], 1), n_kv) : n_kv;
+}
 
 __device__ __forceinline__ int perm_key(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
 
@@ -101,16 +123,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int b = blockIdx.y / a.hkv;
   const int kvh = blockIdx.y % a.hkv;
 
+  const int kpg = kWaves * a.kpw;
+  const int s_len = seq_length(a.seq_lens, b, a.n_kv);
+  const SeqSplit sq = seq_split(s_len, BIF, a.pretrained_window, a.local_window, kpg);
+  if (sp >= sq.n_chunks) return;  // a shorter sequence of the batch: no chunk here
   int ks, ke;
   bool remote = false;
-  const int kpg = kWaves * a.kpw;
-  if (sp < a.n_rem_wg) {
+  if (sp < sq.n_rem) {
     ks = sp * kpg;
-    ke = min(a.remote_end, ks + kpg);
+    ke = min(sq.remote_end, ks + kpg);
     remote = BIF;
   } else {
-    ks = a.remote_end + (sp - a.n_rem_wg) * kpg;
-    ke = min(a.n_kv, ks + kpg);
+    ks = sq.remote_end + (sp - sq.n_rem) * kpg;
+    ke = min(s_len, ks + kpg);
   }
   const int ws = ks + wave * a.kpw;
   const int we = min(ke, ws + a.kpw);
@@ -129,13 +154,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // load, never for the older ones alone.
   const uint32_t row_bytes = (uint32_t)kv_rs * 2u;  // <= 16 MiB (n_kv_heads <= 65536)
   typedef __attribute__((address_space(3))) void lds_void;
+  // The block's rows, its byte count and so its buffer resource are the same for
+  // the whole wave; readfirstlane states it, or the compiler wraps every buffer
+  // load in a loop over the distinct resources it cannot rule out.
   auto rsrc_for = [&](const uint16_t* base, int jb, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
   };
   auto issue_k = [&](int blk, u32x4 (&kr)[8]) {
     const int j0 = ws + blk * kBlk;
-    const int jb = min(j0, we - 1);
-    const uint32_t nbytes = (uint32_t)min(kBlk, we - jb) * row_bytes;
+    const int jb = __builtin_amdgcn_readfirstlane(min(j0, we - 1));
+    const uint32_t nbytes = (uint32_t)__builtin_amdgcn_readfirstlane(min(kBlk, we - jb) * (int)row_bytes);
     const __amdgpu_buffer_rsrc_t krs = rsrc_for(kbase, jb, nbytes);
     const uint32_t ko = (uint32_t)(min(j0 + perm_key(n), we - 1) - jb) * row_bytes + 16u * (uint32_t)h;
 #pragma unroll
@@ -143,8 +171,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   };
   auto issue_v = [&](int blk, int buf) {
     const int j0 = ws + blk * kBlk;
-    const int jb = min(j0, we - 1);
-    const uint32_t nbytes = (uint32_t)min(kBlk, we - jb) * row_bytes;
+    const int jb = __builtin_amdgcn_readfirstlane(min(j0, we - 1));
+    const uint32_t nbytes = (uint32_t)__builtin_amdgcn_readfirstlane(min(kBlk, we - jb) * (int)row_bytes);
     const __amdgpu_buffer_rsrc_t vrs = rsrc_for(vbase, jb, nbytes);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -198,10 +226,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // (u < 512, the longest wave) is exact enough in fp32, and the sum (below 82 revolutions) lies
   // inside the domain of the hardware sine and cosine, which reduce it exactly.
   int r_s = 0;
+  const float inv_g = 1.0f / (float)sq.g;
   if (BIF && remote) {
-    const int p = a.n_kv - 1;
-    const long long cb = ((long long)(ws / a.g) - ws) - ((long long)(p / a.g) - p);
-    r_s = ws % a.g;
+    const int p = s_len - 1;  // the query's position
+    const long long cb = ((long long)(ws / sq.g) - ws) - ((long long)(p / sq.g) - p);
+    r_s = ws % sq.g;
     const double r = (double)cb * th64;
     s_fb[wave][lane] = (float)(r - __builtin_rint(r));
     s_th[wave][lane] = th32;
@@ -230,7 +259,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     __builtin_amdgcn_sched_barrier(0);  // nothing that reads the block may move above the wait
     if (BIF && remote) {
       const int t = j0 + perm_key(n) - ws;
-      const float uf = (float)(t - small_div(r_s + t, a.g, a.inv_g));
+      const float uf = (float)(t - small_div(r_s + t, sq.g, inv_g));
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const float4 fb0 = *reinterpret_cast<const float4*>(&s_fb[wave][16 * kk + 8 * h]);
@@ -377,16 +406,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 constexpr int kCombineThreads = 256;
 constexpr int kCombineLanes = kCombineThreads / 32;
 constexpr int kCombineBatch = 16;
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* part_o, const float* part_lse,
-                                                                         uint16_t* out, float* lse, int n_wg) {
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  const int32_t* seq_lens;
+  int32_t n_kv, hq, n_wg, local_window, kpg, bif;
+  int64_t pretrained_window;
+};
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const CombineArgs ca) {
   __shared__ float4 s_o[kCombineLanes][32];
   __shared__ float s_m[kCombineLanes];
   __shared__ float s_l[kCombineLanes];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int cl = tid >> 5, c4 = tid & 31;
-  const float* pl = part_lse + bh * n_wg;
-  const float* po = part_o + bh * n_wg * kD + 4 * c4;
+  const int n_wg = seq_split(seq_length(ca.seq_lens, (int)(bh / ca.hq), ca.n_kv), ca.bif != 0, ca.pretrained_window,
+                             ca.local_window, ca.kpg).n_chunks;
+  const float* pl = ca.part_lse + bh * ca.n_wg;  // rows of ca.n_wg slots, the first n_wg filled
+  const float* po = ca.part_o + bh * ca.n_wg * kD + 4 * c4;
+  uint16_t* out = ca.out;
+  float* lse = ca.lse;
   float m = -INFINITY, l = 0.0f;
   float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = cl; s0 < n_wg; s0 += kCombineLanes * kCombineBatch) {
@@ -488,15 +529,21 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   a.hkv = p.n_kv_heads;
   a.grp = p.n_q_heads / p.n_kv_heads;
   if (a.grp > kMaxGroup) return hipErrorInvalidValue;
-  a.g = bifocal ? p.group : 1;
-  a.remote_end = bifocal ? p.n_kv - p.local_window : 0;
-  if (a.remote_end < 0) a.remote_end = 0;
+  a.seq_lens = p.seq_lens;
+  a.pretrained_window = bifocal ? p.pretrained_window : 1;
+  a.local_window = bifocal ? p.local_window : 0;
   a.nb = decode_blocks_per_wave(p.batch, p.n_kv, p.n_kv_heads);
   a.kpw = kBlk * a.nb;
   const int32_t chunk = kWaves * a.kpw;
-  a.n_rem_wg = (a.remote_end + chunk - 1) / chunk;
-  a.n_wg = a.n_rem_wg + (p.n_kv - a.remote_end + chunk - 1) / chunk;
-  a.inv_g = 1.0f / (float)a.g;
+  if (p.seq_lens) {
+    a.n_wg = decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);  // any length up to n_kv fits
+  } else {
+    // every sequence holds n_kv keys: exactly its chunks (the kernels' cut, on the host)
+    const int64_t g = bifocal ? (int64_t)(p.n_kv - 1) / p.pretrained_window + 1 : 1;
+    const int32_t remote_end = g > 1 ? p.n_kv - (p.local_window < p.n_kv ? p.local_window : p.n_kv) : 0;
+    const int32_t n_rem = (remote_end + chunk - 1) / chunk;
+    a.n_wg = n_rem + (p.n_kv - remote_end + chunk - 1) / chunk;
+  }
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   // theta_d / (2 pi) for this RoPE base, kept per thread for the next call
   thread_local double cached_base = 0.0;
@@ -513,7 +560,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   const size_t rows = (size_t)p.batch * p.n_q_heads * decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);
   a.part_o = static_cast<float*>(p.workspace);
   a.part_lse = a.part_o + rows * kD;
-  // partials are laid out with the actual chunk count as the row stride
+  // partials: rows of n_wg chunk slots per (sequence, query head)
   if (bifocal)
     hipLaunchKernelGGL((decode_split_kernel<true>), dim3(a.n_wg, p.batch * p.n_kv_heads), dim3(kWaves * 64), 0,
                        stream, a);
@@ -522,8 +569,20 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kCombineThreads), 0, stream, a.part_o, a.part_lse,
-                     a.out, a.lse, a.n_wg);
+  CombineArgs ca;
+  ca.part_o = a.part_o;
+  ca.part_lse = a.part_lse;
+  ca.out = a.out;
+  ca.lse = a.lse;
+  ca.seq_lens = a.seq_lens;
+  ca.n_kv = a.n_kv;
+  ca.hq = a.hq;
+  ca.n_wg = a.n_wg;
+  ca.local_window = a.local_window;
+  ca.kpg = chunk;
+  ca.bif = bifocal ? 1 : 0;
+  ca.pretrained_window = a.pretrained_window;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kCombineThreads), 0, stream, ca);
   return hipGetLastError();
 }
 

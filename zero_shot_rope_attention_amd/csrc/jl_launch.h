@@ -37,9 +37,10 @@ struct DecodeProblem {
   const void* v;
   void* out;
   float* lse;
-  int32_t batch, n_kv, n_q_heads, n_kv_heads;
-  int32_t group;         // g(s); 1 for plain
-  int32_t local_window;  // W clamped to <= n_kv; 0 for plain (no local/remote split)
+  const int32_t* seq_lens;   // device [B] keys per sequence, or null: every sequence holds n_kv keys
+  int32_t batch, n_kv, n_q_heads, n_kv_heads;  // n_kv: cache positions per sequence
+  int64_t pretrained_window;  // L (bifocal); g(s) is taken per sequence in the kernels
+  int32_t local_window;       // W (clamped to each sequence's length in the kernels)
   double rope_base;
   float softmax_scale;
   void* workspace;
