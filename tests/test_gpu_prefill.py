@@ -141,3 +141,34 @@ def test_rows_without_remote_keys_match_plain():
     _, _, out, _ = _run(wid, b, n_q, n_kv, hq, hkv, big_l, w, base)
     _, _, out_p, _ = _run(wid, b, n_q, n_kv, hq, hkv, big_l, w, base, plain=True)
     assert_parity(out[:, :w], out_p[:, :w], "rows p < W vs plain", max_tol=2e-3, mean_tol=1e-4)
+
+
+def test_chunked_prefill_as_the_cache_grows():
+    # A prompt prefilled in chunks against the cache so far: each chunk's queries sit at the
+    # newest positions and g is taken from the length reached (seventnews.com: the factor follows
+    # the current length), so g steps from 1 to 3 across the chunks (L = 512).  Both prefill
+    # forms, each chunk against the oracle at its own length.
+    big_l, w, base, n, hq, hkv = 512, 96, 1e4, 1400, 4, 2
+    qb, kb, vb = make_qkv(140, 1, n, n, hq, hkv, 128)
+    q, k, v = to_device(qb), to_device(kb), to_device(vb)
+    qf, kf, vf = bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+    ws = torch.empty(jl.jl_bifocal_prefill_workspace_size(1, n, hkv), dtype=torch.uint8, device="cuda:0")
+    seen = []
+    for lo, hi in ((0, 300), (300, 513), (513, 700), (700, 1025), (1025, 1400)):
+        qc = q[:, lo:hi].contiguous()
+        kc, vc = k[:, :hi].contiguous(), v[:, :hi].contiguous()
+        ref = oracle.bifocal_three_pass(qf[:, lo:hi], kf[:, :hi], vf[:, :hi], big_l, w, base)
+        seen.append(ref["g"])
+        for form in ("fused", "ws"):
+            out = torch.empty_like(qc)
+            lse = torch.empty((1, hq, hi - lo), dtype=torch.float32, device="cuda:0")
+            print(f"chunk [{lo}, {hi}) g={ref['g']} form={form}", flush=True)
+            if form == "fused":
+                jl.jl_bifocal_prefill(qc, kc, vc, out, lse, big_l, w, base)
+            else:
+                jl.jl_bifocal_prefill_ws(qc, kc, vc, out, lse, big_l, w, base, ws)
+            torch.cuda.synchronize()
+            assert_parity(to_f64(out), ref["out"], f"chunk [{lo}, {hi}) {form}")
+            assert_parity(lse.cpu().numpy().astype(np.float64), ref["lse"], "lse", max_tol=LSE_TOL,
+                          mean_tol=LSE_MEAN_TOL)
+    assert seen == [1, 2, 2, 3, 3]
