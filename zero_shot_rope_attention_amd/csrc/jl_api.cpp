@@ -2,6 +2,7 @@
 // planning and error reporting.  Declarations and contracts: include/jl_bifocal.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -44,12 +45,14 @@ int64_t elements(int64_t b, int64_t n, int64_t h) {
 
 // One query of the HIP runtime per process: is there a usable device?
 jl_status device_check() {
-  static int state = -1;  // -1 unknown, 0 none, 1 present
-  if (state < 0) {
+  static std::atomic<int> state{-1};  // -1 unknown, 0 none, 1 present (callers may race to fill it)
+  int st = state.load(std::memory_order_relaxed);
+  if (st < 0) {
     int count = 0;
-    state = (hipGetDeviceCount(&count) == hipSuccess && count > 0) ? 1 : 0;
+    st = (hipGetDeviceCount(&count) == hipSuccess && count > 0) ? 1 : 0;
+    state.store(st, std::memory_order_relaxed);
   }
-  if (state == 0) return fail(JL_ERR_DEVICE, "no HIP device available");
+  if (st == 0) return fail(JL_ERR_DEVICE, "no HIP device available");
   return JL_OK;
 }
 
