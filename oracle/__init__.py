@@ -40,5 +40,6 @@ from .bifocal import (  # noqa: F401
     bifocal_decode,
     bifocal_decode_varlen,
     plain_decode_varlen,
+    sliding_window_attention,
     merge_passes,
 )

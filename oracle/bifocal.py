@@ -29,6 +29,9 @@ Parity pins (see ``tests/test_oracle_*.py``):
 * ``plain_causal_attention``: torch fp64 ``scaled_dot_product_attention``.
 * ``bifocal_decode``: it is ``bifocal_three_pass`` at one query row, pinned by the
   same tests plus the decode-equals-last-prefill-row check.
+* ``sliding_window_attention``: torch's fp64 ``scaled_dot_product_attention`` with an
+  explicit band mask; equals pass A of ``bifocal_three_pass``; equals
+  ``plain_causal_attention`` when the window covers every key; W = 1 returns v_p.
 * ``bifocal_decode_varlen`` / ``plain_decode_varlen``: each sequence equals
   ``bifocal_bruteforce`` (per-pair position selection, g from that sequence's own
   length) on its own prefix, with the cache rows past the prefix set to NaN; with
@@ -58,6 +61,7 @@ __all__ = [
     "bifocal_decode",
     "bifocal_decode_varlen",
     "plain_decode_varlen",
+    "sliding_window_attention",
     "merge_passes",
 ]
 
@@ -337,6 +341,45 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
 
     out, lse = merge_passes(res["A"][0], res["A"][1], res["B"][0], res["B"][1], res["C"][0], res["C"][1])
     return {"out": out, "lse": lse, "passes": res, "g": g}
+
+
+def sliding_window_attention(q, k, v, local_window, softmax_scale=None, rows=None, row_block=256):
+    """Plain sliding-window attention: query row i (position p_i) attends to the
+    keys j with 0 <= p_i - j <= W - 1, scores tau * q_i . k_j on the cached
+    vectors (base RoPE), one masked softmax per row.
+
+    seventnews.com, "Generalization to hybrid attention architectures": hybrid
+    models keep sliding-window layers next to the global ones.  A window W <= L
+    never leaves the pretrained positions, so those layers run the base model's
+    attention restricted to the window -- the local view (pass A) of the merge.
+    Returns ``(out [B, R, Hq, D], lse [B, Hq, R])`` for the selected rows.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    b, n_q, n_kv, hq, hkv, d = _check_shapes(q, k, v)
+    w_loc = int(local_window)
+    if w_loc < 1:
+        raise ValueError("need local_window >= 1")
+    scale = 1.0 / math.sqrt(d) if not softmax_scale or softmax_scale <= 0 else float(softmax_scale)
+    pos = query_positions(n_q, n_kv)
+    rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    grp = hq // hkv
+    out = np.zeros((b, len(rows), hq, d))
+    lse = np.zeros((b, hq, len(rows)))
+    for bi in range(b):
+        for h in range(hq):
+            kh = h // grp
+            for r0 in range(0, len(rows), row_block):
+                sl = slice(r0, r0 + row_block)
+                p = pos[rows[sl]]
+                lo = max(0, int(p.min()) - w_loc + 1)
+                j = np.arange(lo, int(p.max()) + 1)
+                dist = p[:, None] - j[None, :]
+                band = (dist >= 0) & (dist <= w_loc - 1)
+                s_ = scale * (q[bi, rows[sl], h] @ k[bi, lo:lo + len(j), kh].T)
+                o, l_ = _partial_softmax(s_, band, v[bi, lo:lo + len(j), kh])
+                out[bi, sl, h] = o
+                lse[bi, h, sl] = l_
+    return out, lse
 
 
 # ---------------------------------------------------------------------------

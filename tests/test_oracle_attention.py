@@ -278,3 +278,30 @@ def test_decode_varlen_equals_bruteforce_per_sequence():
         vt = torch.from_numpy(np.repeat(v[bi:bi + 1, :s], hq // hkv, axis=2)).permute(0, 2, 1, 3)
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).permute(0, 2, 1, 3).numpy()
         assert np.abs(out_p[bi:bi + 1] - ref).max() <= 1e-12
+
+
+@pytest.mark.parametrize("n_q,n_kv,w,hq,hkv", [(40, 40, 7, 4, 2), (9, 50, 16, 2, 1), (1, 33, 5, 4, 4), (64, 64, 1, 2, 2)])
+def test_sliding_window_attention_pins(n_q, n_kv, w, hq, hkv):
+    q, k, v = _raw_inputs(7000 + n_kv * 10 + w, 2, n_q, n_kv, hq, hkv, 16)
+    out, lse = oracle.sliding_window_attention(q, k, v, w)
+    # torch's fp64 attention with an explicit band mask (query i at position n_kv - n_q + i)
+    pos = np.arange(n_kv - n_q, n_kv)
+    dist = pos[:, None] - np.arange(n_kv)[None, :]
+    band = torch.from_numpy((dist >= 0) & (dist <= w - 1))
+    rep = hq // hkv
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(np.repeat(k, rep, axis=2)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(np.repeat(v, rep, axis=2)).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=band).permute(0, 2, 1, 3).numpy()
+    assert np.abs(out - ref).max() <= 1e-12
+    # it is the local view (pass A) of the three-pass form, for any L >= W
+    r = oracle.bifocal_three_pass(q, k, v, max(w, 4), w, 1e4)
+    o_a, l_a = r["passes"]["A"]
+    assert np.abs(out - o_a).max() <= 1e-12 and np.abs(lse - l_a).max() <= 1e-12
+    # a window covering every key is plain causal attention
+    o_p, l_p = oracle.plain_causal_attention(q, k, v)
+    o_w, l_w = oracle.sliding_window_attention(q, k, v, n_kv)
+    assert np.abs(o_w - o_p).max() <= 1e-12 and np.abs(l_w - l_p).max() <= 1e-12
+    if w == 1:   # only the query's own key: the output is that key's value
+        for i, p in enumerate(pos):
+            assert np.abs(out[:, i] - np.repeat(v[:, p], rep, axis=1)).max() <= 1e-15
