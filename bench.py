@@ -253,6 +253,41 @@ def main():
         log(f"plain prefill {plain_ms:.2f} ms")
         del out_p
 
+        # sliding-window layers of a hybrid model (window W, base RoPE): prefill and decode at this length;
+        # algorithmic work 4*D*Hq*B*sum_i min(p_i + 1, W)
+        out_s = torch.empty_like(q)
+        for _ in range(2):
+            jl.jl_sliding_prefill(q, k, v, out_s, None, w)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            jl.jl_sliding_prefill(q, k, v, out_s, None, w)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        sl_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        pairs = w * (w + 1) // 2 + (s - w) * w if s >= w else s * (s + 1) // 2
+        sl_flops = 4.0 * 128 * hq * b * pairs
+        out_sd = torch.empty_like(q_dec)
+        sd = []
+        for it in range(args.decode_warmup + args.decode_iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            jl.jl_sliding_decode(q_dec, k, v, out_sd, None, w, ws)
+            e1.record(stream)
+            if it >= args.decode_warmup:
+                sd.append((e0, e1))
+        torch.cuda.synchronize()
+        sd_us = float(np.median([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in sd]))
+        result["sliding_window"] = {
+            "window": w,
+            "prefill": {"ms": round(sl_ms, 4), "tflops": round(sl_flops / (sl_ms * 1e-3) / 1e12, 2),
+                        "flops": sl_flops, "kernel": "prefill_pp_kernel<4>"},
+            "decode": {"us_median": round(sd_us, 2), "kv_bytes": 2 * b * min(w, s) * hkv * 128 * 2},
+        }
+        log(f"sliding window W={w}: prefill {sl_ms:.2f} ms ({sl_flops / (sl_ms * 1e-3) / 1e12:.1f} TFLOP/s), "
+            f"decode {sd_us:.2f} us")
+        del out_s
+
         # decode: one query against caches of 32K, 64K and 128K positions (those up to the workload's
         # length).  Each length rotates among distinct cache slices, 1.5 GiB in total, so that the
         # 256 MB last-level cache cannot serve them; bifocal and plain interleaved in one process.

@@ -127,6 +127,20 @@ jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* ou
                            int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
                            int32_t n_kv_heads, int32_t head_dim, float softmax_scale, void* stream);
 
+/* Sliding-window attention: query row i attends to the keys j with
+ * 0 <= p_i - j <= W-1 on the cached vectors (base RoPE), one softmax per row.
+ * It serves the sliding-window layers of hybrid models, which keep such layers
+ * next to the global ones (seventnews.com, "Generalization to hybrid attention
+ * architectures"): a window W <= L never leaves the pretrained positions, so
+ * those layers need no correction -- it is the local view (pass A) on its own.
+ * Same layouts as jl_bifocal_prefill; local_window >= 1 (a window of at least
+ * n_kv keys is plain causal attention).  Tiles wholly outside every row's
+ * window are not read. */
+jl_status jl_sliding_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int64_t local_window,
+                             float softmax_scale, void* stream);
+
 /* Per-pass results of the three FlashAttention-style passes of the merge
  * (ResearchPod transcript, prefill exchange: local view A, remapped distant
  * view B, corrected local view C), each normalised on its own key set:
@@ -167,6 +181,16 @@ jl_status jl_plain_decode(const void* q, const void* k_cache, const void* v_cach
                           float* lse, int32_t batch, int32_t n_kv, int32_t n_q_heads,
                           int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sliding-window decode: the new token at n_kv-1 attends to the newest
+ * min(W, n_kv) cached keys (base RoPE), read by the split-K kernels; keys older
+ * than the window are never read.  Layouts and workspace as jl_bifocal_decode
+ * (jl_bifocal_decode_workspace_size bytes); local_window >= 1. */
+jl_status jl_sliding_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                            float* lse, int32_t batch, int32_t n_kv, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int64_t local_window,
+                            float softmax_scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Bifocal decode of a batch of sequences of different lengths: one new token
  * per sequence, each against its own cache prefix, with g taken per sequence

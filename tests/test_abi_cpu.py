@@ -154,6 +154,35 @@ def test_decode_varlen_validation(lib):
     assert dec(w=33) == INVALID                            # W > L
 
 
+def test_sliding_validation(lib):
+    def pre(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, batch=1, n_q=64, n_kv=64, hq=4, hkv=2, d=128, w=8,
+                 scale=0.0)
+        a.update(kw)
+        return lib.jl_sliding_prefill(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["n_q"], a["n_kv"],
+                                      a["hq"], a["hkv"], a["d"], a["w"], a["scale"], None)
+
+    need = lib.jl_bifocal_decode_workspace_size(1, 100, 4, 2, 128)
+
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, batch=1, n_kv=100, hq=4, hkv=2, d=128, w=8, scale=0.0,
+                 ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_sliding_decode(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["n_kv"], a["hq"],
+                                     a["hkv"], a["d"], a["w"], a["scale"], a["ws"], a["wsb"], None)
+
+    for call in (pre, dec):
+        assert call(w=0) == INVALID
+        assert call(d=64) == UNSUPPORTED
+        assert call(k=None) == INVALID
+        assert call(hq=3) == INVALID                       # Hq % Hkv != 0
+        if not _has_gpu():
+            assert call() == DEVICE
+            assert call(w=10 ** 6) == DEVICE               # a window wider than the context is fine
+    assert dec(wsb=need - 1) == WORKSPACE
+    assert pre(n_q=65) == INVALID                          # n_q > n_kv
+
+
 def test_prefill_ws_workspace_and_validation(lib):
     # one corrected copy of the keys: B * n_kv * Hkv * 128 bf16
     assert lib.jl_bifocal_prefill_workspace_size(1, 131072, 8, 128) == 131072 * 8 * 128 * 2

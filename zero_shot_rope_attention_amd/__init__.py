@@ -29,6 +29,8 @@ __all__ = [
     "jl_plain_decode",
     "jl_bifocal_decode_varlen",
     "jl_plain_decode_varlen",
+    "jl_sliding_prefill",
+    "jl_sliding_decode",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
@@ -56,6 +58,8 @@ _SIGNATURES = {
                                         _f32, _vp, _sz, _vp]),
     "jl_plain_decode_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz,
                                       _vp]),
+    "jl_sliding_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
+    "jl_sliding_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -207,3 +211,23 @@ def jl_plain_decode_varlen(q, k_cache, v_cache, out, lse, seq_lens, workspace, s
     _check(load_library().jl_plain_decode_varlen(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _seq_lens_ptr(seq_lens), b, n_max, hq, hkv, d,
         float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_sliding_prefill(q, k, v, out, lse, local_window, softmax_scale=0.0, stream=None):
+    """Sliding-window attention over the newest ``local_window`` keys of each
+    query row; layouts as jl_bifocal_prefill."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    _check(load_library().jl_sliding_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq, hkv,
+                                             d, int(local_window), float(softmax_scale), _stream(stream)))
+
+
+def jl_sliding_decode(q, k_cache, v_cache, out, lse, local_window, workspace, softmax_scale=0.0, stream=None):
+    """One new token over the newest ``local_window`` cached keys; workspace as
+    for jl_bifocal_decode."""
+    b, _, hq, d = q.shape
+    n_kv, hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_sliding_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b, n_kv, hq,
+                                            hkv, d, int(local_window), float(softmax_scale), _ptr(workspace), nbytes,
+                                            _stream(stream)))

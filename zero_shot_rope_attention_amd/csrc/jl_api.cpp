@@ -145,6 +145,22 @@ jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* ou
   return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
 }
 
+jl_status jl_sliding_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
+                             int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                             int64_t local_window, float softmax_scale, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  if (local_window < 1) return fail(JL_ERR_INVALID_ARG, "local_window must be >= 1 (got %lld)", (long long)local_window);
+  JL_TRY(device_check());
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, w,
+                       2.0, scale};
+  return launched(jl::launch_prefill(jl::kModeSliding, p, static_cast<hipStream_t>(stream)));
+}
+
 jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
                              int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                              int64_t pretrained_window, int64_t local_window, double rope_base,
@@ -265,6 +281,22 @@ jl_status jl_bifocal_decode(const void* q, const void* k_cache, const void* v_ca
   jl::DecodeProblem p{q, k_cache, v_cache, out, lse, nullptr, batch, n_kv, n_q_heads, n_kv_heads, pretrained_window,
                       w, rope_base, scale, workspace};
   return launched(jl::launch_decode(g > 1, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_sliding_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                            int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int64_t local_window, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  if (local_window < 1) return fail(JL_ERR_INVALID_ARG, "local_window must be >= 1 (got %lld)", (long long)local_window);
+  JL_TRY(device_check());
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, nullptr, batch, n_kv, n_q_heads, n_kv_heads, 1, w, 2.0, scale,
+                      workspace};
+  p.sliding = true;
+  return launched(jl::launch_decode(false, p, static_cast<hipStream_t>(stream)));
 }
 
 static jl_status check_seq_lens(const int32_t* seq_lens) {

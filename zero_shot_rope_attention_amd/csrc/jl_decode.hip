@@ -55,6 +55,7 @@ struct DecodeArgs {
   int32_t nb;          // 32-key blocks per wave (even, 2..16)
   int32_t kpw;         // keys per wave = 32 nb; a chunk is kWaves * kpw keys
   int32_t order_ncu;   // > 0: workgroup order interleaves heads with this stride (the CU count); 0: chunk-major
+  int32_t sliding;     // 1: sliding window, only the newest min(W, s) keys (plain kernel)
   float scale_log2;
   float theta_rev32[kHalfD];
   double theta_rev[kHalfD];
@@ -64,15 +65,17 @@ struct DecodeArgs {
 // plain); with g > 1 the remote prefix [0, s - min(W, s)) is cut into n_rem
 // chunks of kpg keys and the local suffix into the rest, so that no chunk
 // straddles the boundary; with g = 1 every chunk is local (base scores).
+// A sliding window (plain attention over the newest min(W, s) keys) has no
+// remote chunk at all: only the suffix is cut, with base scores.
 struct SeqSplit {
   int g, remote_end, n_rem, n_chunks;
 };
-__device__ __forceinline__ SeqSplit seq_split(int s, bool bif, int64_t big_l, int w_req, int kpg) {
+__device__ __forceinline__ SeqSplit seq_split(int s, bool bif, int64_t big_l, int w_req, int kpg, bool sliding) {
   SeqSplit r;
   r.g = bif ? (int)((int64_t)(s - 1) / big_l + 1) : 1;  // smallest g with floor((s-1)/g) <= L-1
   const int w = min(w_req, s);
-  r.remote_end = r.g > 1 ? s - w : 0;
-  r.n_rem = (r.remote_end + kpg - 1) / kpg;
+  r.remote_end = (r.g > 1 || sliding) ? s - w : 0;
+  r.n_rem = sliding ? 0 : (r.remote_end + kpg - 1) / kpg;
   r.n_chunks = r.n_rem + (s - r.remote_end + kpg - 1) / kpg;
   return r;
 }
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int kpg = kWaves * a.kpw;
   const int s_len = seq_length(a.seq_lens, b, a.n_kv);
-  const SeqSplit sq = seq_split(s_len, BIF, a.pretrained_window, a.local_window, kpg);
+  const SeqSplit sq = seq_split(s_len, BIF, a.pretrained_window, a.local_window, kpg, a.sliding != 0);
   if (sp >= sq.n_chunks) return;  // a shorter sequence of the batch: no chunk here
   int ks, ke;
   bool remote = false;
@@ -433,7 +436,7 @@ struct CombineArgs {
   uint16_t* out;
   float* lse;
   const int32_t* seq_lens;
-  int32_t n_kv, hq, n_wg, local_window, kpg, bif;
+  int32_t n_kv, hq, n_wg, local_window, kpg, bif, sliding;
   int64_t pretrained_window;
 };
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const CombineArgs ca) {
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const C
   const int tid = threadIdx.x;
   const int cl = tid >> 5, c4 = tid & 31;
   const int n_wg = seq_split(seq_length(ca.seq_lens, (int)(bh / ca.hq), ca.n_kv), ca.bif != 0, ca.pretrained_window,
-                             ca.local_window, ca.kpg).n_chunks;
+                             ca.local_window, ca.kpg, ca.sliding != 0).n_chunks;
   const float* pl = ca.part_lse + bh * ca.n_wg;  // rows of ca.n_wg slots, the first n_wg filled
   const float* po = ca.part_o + bh * ca.n_wg * kD + 4 * c4;
   uint16_t* out = ca.out;
@@ -566,13 +569,25 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   a.grp = p.n_q_heads / p.n_kv_heads;
   if (a.grp > kMaxGroup) return hipErrorInvalidValue;
   a.seq_lens = p.seq_lens;
+  a.sliding = p.sliding ? 1 : 0;
+  if (p.sliding && bifocal) return hipErrorInvalidValue;
   a.pretrained_window = bifocal ? p.pretrained_window : 1;
-  a.local_window = bifocal ? p.local_window : 0;
+  a.local_window = (bifocal || p.sliding) ? p.local_window : 0;
   a.nb = decode_blocks_per_wave(p.batch, p.n_kv, p.n_kv_heads);
+  if (p.sliding) {
+    // chunks sized for the window's keys, if their count fits the workspace bound
+    const int32_t w = p.local_window < p.n_kv ? p.local_window : p.n_kv;
+    const int32_t nb_w = decode_blocks_per_wave(p.batch, w, p.n_kv_heads);
+    const int32_t chunk_w = kWaves * kBlk * nb_w;
+    if ((w + chunk_w - 1) / chunk_w <= decode_max_splits(p.batch, p.n_kv, p.n_kv_heads)) a.nb = nb_w;
+  }
   a.kpw = kBlk * a.nb;
   const int32_t chunk = kWaves * a.kpw;
   if (p.seq_lens) {
     a.n_wg = decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);  // any length up to n_kv fits
+  } else if (p.sliding) {
+    const int32_t w = p.local_window < p.n_kv ? p.local_window : p.n_kv;
+    a.n_wg = (w + chunk - 1) / chunk;
   } else {
     // every sequence holds n_kv keys: exactly its chunks (the kernels' cut, on the host)
     const int64_t g = bifocal ? (int64_t)(p.n_kv - 1) / p.pretrained_window + 1 : 1;
@@ -622,6 +637,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   ca.local_window = a.local_window;
   ca.kpg = chunk;
   ca.bif = bifocal ? 1 : 0;
+  ca.sliding = a.sliding;
   ca.pretrained_window = a.pretrained_window;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kCombineThreads), 0, stream, ca);
   return hipGetLastError();

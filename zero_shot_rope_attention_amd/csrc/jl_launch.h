@@ -10,7 +10,7 @@ namespace jl {
 // kModeBifocal corrects the keys tile by tile inside the attention kernel;
 // kModeBifocalPre first writes the corrected keys of the whole cache to a
 // workspace (one elementwise pass) and stages them like plain keys.
-enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2, kModeBifocalPre = 3 };
+enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2, kModeBifocalPre = 3, kModeSliding = 4 };
 
 // Everything a prefill launch needs; validated by the caller.
 struct PrefillProblem {
@@ -44,6 +44,7 @@ struct DecodeProblem {
   double rope_base;
   float softmax_scale;
   void* workspace;
+  bool sliding = false;  // plain attention over the newest min(W, s) keys only (bifocal must be false)
 };
 
 // Number of key chunks the decode splits a cache of n_kv keys into (upper bound

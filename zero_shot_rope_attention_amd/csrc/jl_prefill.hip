@@ -797,9 +797,10 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
 
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
-  static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre,
-                "ping-pong kernel: plain or bifocal");
-  constexpr bool kGrouped = MODE != kModePlain;     // grouped scores on remote keys
+  static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre || MODE == kModeSliding,
+                "ping-pong kernel: plain, bifocal or sliding window");
+  constexpr bool kSliding = MODE == kModeSliding;   // base scores on the window's keys only
+  constexpr bool kGrouped = MODE != kModePlain && !kSliding;  // grouped scores on remote keys
   constexpr bool kRotate = MODE == kModeBifocal;    // keys corrected here, tile by tile
   constexpr bool kPre = MODE == kModeBifocalPre;    // keys corrected beforehand (a.kg)
   constexpr int kTileBytes = kBN * 256;
@@ -861,9 +862,13 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   int n_interior = 0;
   if constexpr (MODE == kModePlain) n_interior = min(ntiles, max(0, (p0_wg + 1) / kBN));
   if constexpr (kGrouped) n_interior = min(ntiles, max(0, (p0_wg - a.w + 1) / kBN));
+  // sliding window: the sweep starts at the first tile holding a key inside
+  // some row's window; the tiles before it are never read.  t0 is 0 otherwise.
+  const int t0 = kSliding ? min(ntiles - 1, max(0, (p0_wg - a.w + 1) / kBN)) : 0;
+  if constexpr (kSliding) n_interior = t0;
   // first tile whose causal keys are local for every row of the workgroup
   int t_local = n_interior;
-  if constexpr (kGrouped) {
+  if constexpr (kGrouped || kSliding) {
     const int first_all_local = pos_off + last_row_wg - a.w + 1;
     t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
     t_local = min(ntiles, max(n_interior, t_local));
@@ -881,7 +886,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   }
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
-  load_half(regs, k_src(0), vbase, kv_rs, a.n_kv, 0, soff);
+  load_half(regs, k_src(t0), vbase, kv_rs, a.n_kv, t0 * kBN, soff);
 
   bf16x8 qf[8];
   bf16x8 qg[8];
@@ -947,15 +952,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     }
     __syncthreads();
   }
-  store(0, 2 * grp);
+  store(t0, 2 * grp);
   __syncthreads();
-  if (ntiles > 1) {
+  if (ntiles > t0 + 1) {
     if constexpr (kRotate) {
       if (gtid < 64) base_angles(1, 2 * grp);
       __syncthreads();
     }
-    load_half(regs, k_src(1), vbase, kv_rs, a.n_kv, kBN, soff);
-    store(1, 2 * grp);
+    load_half(regs, k_src(t0 + 1), vbase, kv_rs, a.n_kv, (t0 + 1) * kBN, soff);
+    store(t0 + 1, 2 * grp);
   }
   if constexpr (kRotate) {
     __syncthreads();
@@ -972,7 +977,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[0][nb] = f32x16{};
 
-  auto uses = [&](int t) { return wave_rows && t * kBN <= wp_hi; };
+  // tile t holds a key this wave's rows attend to (sliding: inside some row's window)
+  auto uses = [&](int t) {
+    return wave_rows && t * kBN <= wp_hi && (!kSliding || t * kBN + kBN - 1 >= wp_lo - a.w + 1);
+  };
 
   float xs[1][2][16];
   uint32_t pk[1][2][8];
@@ -997,7 +1005,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // the wave in its MFMA phase goes first when both waves of a SIMD can issue
     __builtin_amdgcn_s_setprio(2);
     const int tt = k + ahead;
-    const bool do_stage = tt < ntiles && tt >= 2;
+    const bool do_stage = tt < ntiles && tt >= t0 + 2;
     // plain and precorrected: the staging loads fly during the MFMA phase; fused
     // bifocal: they are issued at the start of the VALU phase, so that the 16
     // registers they fill are not live across the MFMA phase, where that kernel
@@ -1005,9 +1013,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     if (!kRotate && do_stage) load_half(regs, k_src(tt), vbase, kv_rs, a.n_kv, tt * kBN, soff);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
-    // V of tile k-1 (at k = 0 the probabilities are zero and tile 0's finite V
-    // is read instead, which adds exactly nothing)
-    const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) % 3) * kTileBytes;
+    // V of tile k-1 (at the first tile the probabilities are zero and that
+    // tile's finite V is read instead, which adds exactly nothing)
+    const uint8_t* svp = s_v + ((k > t0 ? k - 1 : t0) % 3) * kTileBytes;
     if constexpr (kKind == kInterior) {
       f32x16 sc[2];
       mphase_interior<true>(kGrouped ? skg : sk, svp, lofs, kGrouped ? qg : qf, pk, sc, acc);
@@ -1019,14 +1027,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       const int j0 = k * kBN;
       if (uses(k)) {
         if constexpr (kKind == kEdge) {
-          const bool use_grp = (j0 <= wp_hi - a.w);
+          // sliding window: keys outside every window are masked, not grouped
+          const bool use_grp = !kSliding && (j0 <= wp_hi - a.w);
           const bool use_base = (j0 + kBN - 1 >= wp_lo - a.w + 1);
           tile_scores<kModeBifocal, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, use_base, use_grp, xs);
         } else {
           tile_scores<kModePlain, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, a.w, true, false, xs);
         }
       }
-      if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
+      if (k > t0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
     }
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
@@ -1063,16 +1072,18 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     __syncthreads();
   };
 
-  int k = 0;
-  for (; k < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{});
+  int k = t0;
+  if constexpr (!kSliding)
+    for (; k < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{});
   if constexpr (kGrouped) {
     // the base-RoPE query fragment is only needed from the band on
     const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
-    for (; k < t_local; ++k) tile(k, std::integral_constant<int, kEdge>{});
   }
+  if constexpr (kGrouped || kSliding)
+    for (; k < t_local; ++k) tile(k, std::integral_constant<int, kEdge>{});
   for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{});
   if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lofs, pk, acc);
   if (grp == 0) __syncthreads();
@@ -1204,6 +1215,7 @@ hipError_t launch_prefill(PrefillMode mode, const PrefillProblem& p, hipStream_t
     case kModeBifocal: return launch_mode<kModeBifocal, 8>(p, stream);
     case kModePasses: return launch_mode<kModePasses, 4>(p, stream);
     case kModeBifocalPre: return launch_mode<kModeBifocalPre, 8>(p, stream);
+    case kModeSliding: return launch_mode<kModeSliding, 8>(p, stream);
   }
   return hipErrorInvalidValue;
 }
