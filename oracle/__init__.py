@@ -41,5 +41,9 @@ from .bifocal import (  # noqa: F401
     bifocal_decode_varlen,
     plain_decode_varlen,
     sliding_window_attention,
+    SCHEDULES,
+    seam_group_factor,
+    fractional_factor,
+    long_range_schedule,
     merge_passes,
 )

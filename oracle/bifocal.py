@@ -29,6 +29,10 @@ Parity pins (see ``tests/test_oracle_*.py``):
 * ``plain_causal_attention``: torch fp64 ``scaled_dot_product_attention``.
 * ``bifocal_decode``: it is ``bifocal_three_pass`` at one query row, pinned by the
   same tests plus the decode-equals-last-prefill-row check.
+* ``long_range_schedule`` (seam-shifted and fractional variants): the three-pass
+  form equals the brute force under each schedule; every schedule recovers the
+  base model when s <= L; the factors are minimal by exhaustive check (parity of
+  the variants' readings themselves unpinned: the pages print no value for them).
 * ``sliding_window_attention``: torch's fp64 ``scaled_dot_product_attention`` with an
   explicit band mask; equals pass A of ``bifocal_three_pass``; equals
   ``plain_causal_attention`` when the window covers every key; W = 1 returns v_p.
@@ -62,6 +66,10 @@ __all__ = [
     "bifocal_decode_varlen",
     "plain_decode_varlen",
     "sliding_window_attention",
+    "SCHEDULES",
+    "seam_group_factor",
+    "fractional_factor",
+    "long_range_schedule",
     "merge_passes",
 ]
 
@@ -108,6 +116,65 @@ def correction_offset(p, g: int):
     applied at lookup)."""
     p = np.asarray(p, dtype=np.int64)
     return p // int(g) - p
+
+
+SCHEDULES = ("grouped", "seam", "fractional")
+
+
+def seam_group_factor(seq_len: int, pretrained_window: int, local_window: int) -> int:
+    """g for the seam-shifted grouping, by direct search: the smallest integer
+    g >= 1 with ``(s-1) // g + W - W // g <= L - 1``, i.e. every remote query/key
+    distance, shifted so that it continues the local window's distances at the
+    seam, stays inside the pretrained positions.  Raises if no g does (W >= L
+    with s > L)."""
+    s, big_l, w = int(seq_len), int(pretrained_window), int(local_window)
+    if s < 1 or big_l < 1 or w < 1:
+        raise ValueError("sizes must be >= 1")
+    for g in range(1, max(s, w) + 2):
+        if (s - 1) // g + w - w // g <= big_l - 1:
+            return g
+    raise ValueError("no seam-shifted grouping keeps the distances inside the window (needs W < L)")
+
+
+def fractional_factor(seq_len: int, pretrained_window: int) -> float:
+    """l for the fractional scaling: the smallest real l >= 1 with
+    ``(s - 1) / l <= L - 1``, the real-valued counterpart of the smallest integer
+    grouping (seventnews.com, 1st section: a rescaling factor l(s) that follows
+    the current length).  Needs L >= 2."""
+    s, big_l = int(seq_len), int(pretrained_window)
+    if s < 1 or big_l < 2:
+        raise ValueError("need seq_len >= 1 and pretrained_window >= 2")
+    return max(1.0, (s - 1) / (big_l - 1))
+
+
+def long_range_schedule(seq_len: int, pretrained_window: int, local_window: int, schedule: str = "grouped"):
+    """The positions a remote query and key are moved to, for one schedule.
+
+    Returns ``(factor, a_q, a_k)``: the factor (integer g, or real l) and two
+    functions mapping original positions to the positions used on the
+    long-range branch.  The local branch always keeps the original positions.
+
+    * ``grouped`` (the reading used everywhere else): a(p) = p // g on both sides
+      (ResearchPod summary, 2nd paragraph: smallest integer grouping).
+    * ``seam``: keys at j // g, queries at p // g + W - W // g.  The shift makes a
+      remote distance continue the local window's distances at the seam; g grows
+      to keep the shifted distances inside L.
+    * ``fractional``: a(p) = p / l on both sides, the scaling read as a real
+      factor (seventnews.com, 1st section; transform-ai's frequencies scaled
+      dynamically).
+    """
+    if schedule == "grouped":
+        g = group_factor(seq_len, pretrained_window)
+        return g, (lambda p: np.asarray(p, dtype=np.int64) // g), (lambda j: np.asarray(j, dtype=np.int64) // g)
+    if schedule == "seam":
+        g = seam_group_factor(seq_len, pretrained_window, local_window)
+        shift = int(local_window) - int(local_window) // g
+        return (g, (lambda p: np.asarray(p, dtype=np.int64) // g + shift),
+                (lambda j: np.asarray(j, dtype=np.int64) // g))
+    if schedule == "fractional":
+        lf = fractional_factor(seq_len, pretrained_window)
+        return lf, (lambda p: np.asarray(p, dtype=np.float64) / lf), (lambda j: np.asarray(j, dtype=np.float64) / lf)
+    raise ValueError(f"unknown schedule {schedule!r}")
 
 
 def query_positions(n_q: int, n_kv: int) -> np.ndarray:
@@ -271,7 +338,7 @@ def plain_causal_attention(q, k, v, softmax_scale=None, rows=None, row_block=256
 # ---------------------------------------------------------------------------
 
 def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
-                       softmax_scale=None, rows=None, row_block=128):
+                       softmax_scale=None, rows=None, row_block=128, schedule="grouped"):
     """Bifocal attention as three FlashAttention-style passes and their merge.
 
     ResearchPod summary, 2nd paragraph (three passes, smallest integer grouping);
@@ -292,11 +359,13 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
 
     Readings: absolute-position aliasing a(p) = p // g on both sides; no seam
     shift; g from s = n_kv; local iff p_i - j <= W - 1; tau = 1/sqrt(D) unless
-    given; GQA head h -> KV head h // (Hq/Hkv).
+    given; GQA head h -> KV head h // (Hq/Hkv).  ``schedule`` selects another
+    long-range schedule (``long_range_schedule``): the corrections become
+    rot(q, (a_q(p) - p) theta) and rot(k, (a_k(j) - j) theta).
 
     Returns a dict with ``out [B, R, Hq, D]``, ``lse [B, Hq, R]`` (natural log),
     ``passes`` = {"A": (O, lse), "B": ..., "C": ...} with the same shapes, and
-    ``g``.
+    ``g`` (the schedule's factor).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     b, n_q, n_kv, hq, hkv, d = _check_shapes(q, k, v)
@@ -305,7 +374,7 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
     if w_loc < 1 or big_l < 1 or w_loc > big_l:
         raise ValueError("need 1 <= local_window <= pretrained_window")
     scale = 1.0 / math.sqrt(d) if not softmax_scale or softmax_scale <= 0 else float(softmax_scale)
-    g = group_factor(n_kv, big_l)
+    g, a_q, a_k = long_range_schedule(n_kv, big_l, w_loc, schedule)
     theta = rope_frequencies(d, rope_base)
     pos = query_positions(n_q, n_kv)
     rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -313,10 +382,12 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
 
     # Correction rotations applied to the cached vectors (on the fly in the method).
     kpos = np.arange(n_kv, dtype=np.int64)
-    k_g = rotate_half_pairs(k, (correction_offset(kpos, g).astype(np.float64)[:, None] * theta)[None, :, None, :])
+    k_corr = (a_k(kpos) - kpos).astype(np.float64)
+    k_g = rotate_half_pairs(k, (k_corr[:, None] * theta)[None, :, None, :])
     q_sel_pos = pos[rows]
     q_sel = q[:, rows]
-    q_g = rotate_half_pairs(q_sel, (correction_offset(q_sel_pos, g).astype(np.float64)[:, None] * theta)[None, :, None, :])
+    q_corr = (a_q(q_sel_pos) - q_sel_pos).astype(np.float64)
+    q_g = rotate_half_pairs(q_sel, (q_corr[:, None] * theta)[None, :, None, :])
 
     nr = len(rows)
     res = {x: (np.zeros((b, nr, hq, d)), np.zeros((b, hq, nr))) for x in "ABC"}
@@ -395,7 +466,7 @@ def _default_selection(g: int, local_window: int):
 
 
 def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_base,
-                       softmax_scale=None, select=None):
+                       softmax_scale=None, select=None, schedule="grouped"):
     """Bifocal attention written as one masked softmax with a per-pair choice of
     positions, on *raw* (un-rotated) q and k.  Pure Python loops over pairs and
     explicit D x D rotation matrices; for tiny inputs only.
@@ -409,14 +480,23 @@ def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_ba
     row, output ``sum_j P_ij v_j``.
 
     ``select(p, j) -> (P_q, P_k)`` replaces the rule (tests use it to plant
-    mistakes); by default the rule above with g = g(n_kv).
+    mistakes); by default the rule above with g = g(n_kv), or the remote
+    positions (a_q(p), a_k(j)) of another ``schedule``.
     Returns ``(out [B, n_q, Hq, D], lse [B, Hq, n_q])``.
     """
     q_raw, k_raw, v = _as_f64(q_raw), _as_f64(k_raw), _as_f64(v)
     b, n_q, n_kv, hq, hkv, d = _check_shapes(q_raw, k_raw, v)
     scale = 1.0 / math.sqrt(d) if not softmax_scale or softmax_scale <= 0 else float(softmax_scale)
-    if select is None:
+    if select is None and schedule == "grouped":
         select = _default_selection(group_factor(n_kv, pretrained_window), int(local_window))
+    elif select is None:
+        _, a_q, a_k = long_range_schedule(n_kv, pretrained_window, local_window, schedule)
+        w_loc = int(local_window)
+
+        def select(p: int, j: int):
+            if p - j <= w_loc - 1:
+                return p, j
+            return float(a_q(p)), float(a_k(j))
     theta = rope_frequencies(d, rope_base)
     pos = query_positions(n_q, n_kv)
     grp = hq // hkv
@@ -424,7 +504,7 @@ def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_ba
 
     def rmat(position):
         if position not in mats:
-            mats[position] = rotation_matrix(position * theta)
+            mats[position] = rotation_matrix(float(position) * theta)
         return mats[position]
 
     out = np.zeros((b, n_q, hq, d))
@@ -439,8 +519,8 @@ def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_ba
                     if j > p:
                         continue
                     pq, pk = select(p, j)
-                    qr = rmat(int(pq)) @ q_raw[bi, i, h]
-                    kr = rmat(int(pk)) @ k_raw[bi, j, kh]
+                    qr = rmat(pq) @ q_raw[bi, i, h]
+                    kr = rmat(pk) @ k_raw[bi, j, kh]
                     row[j] = scale * float(qr @ kr)
                 m = row.max()
                 e = np.exp(row - m)
@@ -456,7 +536,7 @@ def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_ba
 # ---------------------------------------------------------------------------
 
 def bifocal_decode(q, k_cache, v_cache, pretrained_window, local_window, rope_base,
-                   softmax_scale=None):
+                   softmax_scale=None, schedule="grouped"):
     """One generated token attending to a cache of n_kv keys that already holds
     its own key/value (ResearchPod transcript, cache exchange: original
     positions are stored; the correction happens at lookup).
@@ -469,7 +549,7 @@ def bifocal_decode(q, k_cache, v_cache, pretrained_window, local_window, rope_ba
     if q.shape[1] != 1:
         raise ValueError("decode takes one query row")
     r = bifocal_three_pass(q, k_cache, v_cache, pretrained_window, local_window, rope_base,
-                           softmax_scale=softmax_scale)
+                           softmax_scale=softmax_scale, schedule=schedule)
     return r["out"], r["lse"]
 
 

@@ -305,3 +305,111 @@ def test_sliding_window_attention_pins(n_q, n_kv, w, hq, hkv):
     if w == 1:   # only the query's own key: the output is that key's value
         for i, p in enumerate(pos):
             assert np.abs(out[:, i] - np.repeat(v[:, p], rep, axis=1)).max() <= 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Long-range schedule variants: seam-shifted grouping and fractional scaling
+# (seventnews.com, 1st section: l(s) follows the current length; the pages also
+# speak of realigning the two branches at the seam).  The pages print no value
+# for either variant, so these pins check the two formulations against each
+# other and against what the definitions fix.
+
+def _schedule_grid():
+    # (s, n_q, L, W, D, hq, hkv, base); seam needs W < L, fractional L >= 2
+    return [(7, 7, 3, 2, 8, 1, 1, 1e4), (16, 16, 4, 2, 8, 1, 1, 1e4), (33, 33, 16, 8, 8, 1, 1, 1e4),
+            (64, 64, 16, 4, 16, 4, 2, 1e6), (100, 100, 32, 8, 8, 1, 1, 1e4), (65, 9, 16, 15, 16, 2, 1, 1e4),
+            (40, 1, 8, 3, 128, 2, 2, 1e4), (128, 128, 9, 8, 8, 1, 1, 1e4)]
+
+
+@pytest.mark.parametrize("schedule", ["seam", "fractional"])
+@pytest.mark.parametrize("s,n_q,big_l,w,d,hq,hkv,base", _schedule_grid())
+def test_schedule_three_pass_equals_bruteforce(schedule, s, n_q, big_l, w, d, hq, hkv, base):
+    q_raw, k_raw, v = _raw_inputs(s * 77 + w, 1, n_q, s, hq, hkv, d)
+    q, k = _prerotate(q_raw, k_raw, base)
+    r = oracle.bifocal_three_pass(q, k, v, big_l, w, base, schedule=schedule)
+    o2, lse2 = oracle.bifocal_bruteforce(q_raw, k_raw, v, big_l, w, base, schedule=schedule)
+    assert np.abs(r["out"] - o2).max() <= 1e-12 * max(1.0, np.abs(v).max())
+    assert np.abs(r["lse"] - lse2).max() <= 1e-11
+    # and the variant is a different attention from the integer grouping once s > L
+    base_out = oracle.bifocal_three_pass(q, k, v, big_l, w, base)["out"]
+    assert np.abs(r["out"] - base_out).max() > 1e-6
+
+
+@pytest.mark.parametrize("schedule", list(oracle.SCHEDULES))
+@pytest.mark.parametrize("s,big_l,w", [(40, 40, 8), (33, 64, 4), (16, 17, 16)])
+def test_schedules_recover_base_model(schedule, s, big_l, w):
+    # s <= L: every schedule leaves the positions alone (g = 1, no shift; l = 1)
+    q, k, v = _raw_inputs(5 * s + w, 2, s, s, 4, 2, 16)
+    r = oracle.bifocal_three_pass(q, k, v, big_l, w, 1e4, schedule=schedule)
+    o_p, l_p = oracle.plain_causal_attention(q, k, v)
+    assert r["g"] == 1
+    assert np.abs(o_p - _torch_causal(q, k, v, 0.25)).max() < 1e-12
+    assert np.abs(r["out"] - o_p).max() <= 1e-12 and np.abs(r["lse"] - l_p).max() <= 1e-12
+
+
+@pytest.mark.parametrize("s,big_l,w", [(s, big_l, w) for s in (1, 2, 9, 50, 257, 1000)
+                                       for big_l in (2, 3, 8, 33) for w in (1, 2, 7, 32) if w < big_l])
+def test_seam_factor_minimal_over_all_pairs(s, big_l, w):
+    # brute force over every remote (query, key) pair of a length-s input: the
+    # largest shifted distance fits in the window for g, and not for g - 1
+    def max_remote_distance(g):
+        shift = w - w // g
+        return max((p // g + shift - j // g for p in range(s) for j in range(0, p - w + 1)), default=0)
+
+    g, a_q, a_k = oracle.long_range_schedule(s, big_l, w, "seam")
+    assert g == oracle.seam_group_factor(s, big_l, w)
+    p = np.arange(s)
+    remote = [(pp, j) for pp in range(s) for j in range(0, pp - w + 1)]
+    if remote:
+        pq = np.array([r[0] for r in remote])
+        pk = np.array([r[1] for r in remote])
+        assert (a_q(pq) - a_k(pk)).max() == max_remote_distance(g) <= big_l - 1
+    assert np.array_equal(a_k(p), p // g)
+    if g > 1 and s > w:
+        assert max_remote_distance(g - 1) > big_l - 1
+
+
+# g worked out by hand: e.g. s = 40, L = 8, W = 5 needs floor(39/g) - floor(5/g) <= 2,
+# which g = 13 misses (3) and g = 14 meets; at the 128K workload g goes 4 -> 5.
+@pytest.mark.parametrize("s,big_l,w,g_expect", [(40, 8, 5, 14), (200, 16, 5, 19), (1000, 64, 16, 21),
+                                                (131072, 32768, 4096, 5), (131072, 32768, 1, 5)])
+def test_seam_distances_continue_the_window(s, big_l, w, g_expect):
+    # p - j = W (the first remote key): the shifted distance is W or W + 1, so it
+    # continues the local distances 0..W-1; the unshifted grouping gives about W / g
+    g, a_q, a_k = oracle.long_range_schedule(s, big_l, w, "seam")
+    assert g == g_expect
+    j = np.arange(0, s - w)
+    dists = set((a_q(j + w) - a_k(j)).tolist())
+    assert dists <= {w, w + 1} and w in dists
+    # deeper remote keys are farther: distance never decreases as j moves back
+    d_all = a_q(np.full(s - w, s - 1)) - a_k(np.arange(s - w))
+    assert np.all(np.diff(d_all) <= 0)
+    if g > 1 and w >= g:
+        g0, aq0, ak0 = oracle.long_range_schedule(s, big_l, w, "grouped")
+        assert (aq0(j + w) - ak0(j)).max() <= w // g0 + 1 < w
+
+
+def test_fractional_two_dim_closed_form():
+    # D = 2: one rotate-half pair with theta_0 = 1.  s = 7, L = 3 -> l = 3; W = 2.
+    # Remote pairs see the positions p / l and j / l, local pairs p and j.
+    rng = np.random.default_rng(12)
+    s, big_l, w = 7, 3, 2
+    lf = oracle.fractional_factor(s, big_l)
+    assert lf == 3.0
+    r_q, a_q = rng.uniform(0.5, 2.0, s), rng.uniform(-3, 3, s)
+    r_k, a_k = rng.uniform(0.5, 2.0, s), rng.uniform(-3, 3, s)
+    v = rng.standard_normal((1, s, 1, 2))
+    tau = 1.0 / math.sqrt(2.0)
+    expected = np.zeros((s, 2))
+    for p in range(s):
+        sc = []
+        for j in range(p + 1):
+            pq, pk = (p, j) if p - j <= w - 1 else (p / 3.0, j / 3.0)
+            sc.append(tau * r_q[p] * r_k[j] * math.cos((a_q[p] + pq) - (a_k[j] + pk)))
+        sc = np.array(sc)
+        e = np.exp(sc - sc.max())
+        expected[p] = (e / e.sum()) @ v[0, :p + 1, 0]
+    q = np.array([[r_q[p] * math.cos(a_q[p] + p), r_q[p] * math.sin(a_q[p] + p)] for p in range(s)])
+    k = np.array([[r_k[j] * math.cos(a_k[j] + j), r_k[j] * math.sin(a_k[j] + j)] for j in range(s)])
+    r = oracle.bifocal_three_pass(q[None, :, None], k[None, :, None], v, big_l, w, 1e4, schedule="fractional")
+    assert np.abs(r["out"][0, :, 0] - expected).max() <= 1e-12
