@@ -17,8 +17,10 @@ Printed (one JSON line): prefill TFLOP/s on the algorithmic count
 peak 2.5 PFLOP/s); decode HBM GB/s over the K+V bytes at caches of 32K, 64K
 and 128K positions (cache slices rotated so the 256 MB last-level cache cannot
 hold them) and its overhead vs the plain decode built the same way; the plain
-causal prefill for comparison; and the fp64 CPU oracle timed on a bounded sample
-of rows.
+causal prefill for comparison; the sliding-window layers of hybrid models; a
+batch of 8 sequences of different lengths; the prefill and decode under each
+long-range schedule (integer grouping, seam-shifted grouping, fractional
+scaling); and the fp64 CPU oracle timed on a bounded sample of rows.
 """
 
 from __future__ import annotations
@@ -340,6 +342,40 @@ def main():
         if sweep and sweep[-1]["n_kv"] == s:
             result["decode"] = dict(sweep[-1])  # the workload's own length
         result["decode_sweep"] = sweep
+
+        # long-range schedules (integer grouping, seam-shifted grouping, fractional scaling): the
+        # two-launch prefill and the decode at the workload's length, timed like the lines above
+        scheds = {}
+        for name in ("grouped", "seam", "fractional"):
+            jl.jl_bifocal_prefill_sched(q, k, v, out, lse, big_l, w, base, name, ws_pre)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for e in ev:
+                e[0].record(stream)
+                jl.jl_bifocal_prefill_sched(q, k, v, out, lse, big_l, w, base, name, ws_pre)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            sp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+            per = []
+            n_it = args.decode_warmup + args.decode_iters // 2
+            for it in range(n_it):
+                if it % batch_iters == 0:
+                    torch.cuda._sleep(spin_cycles)
+                kc, vc = caches[it % len(caches)]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                jl.jl_bifocal_decode_sched(q_dec, kc, vc, out_dec, None, None, big_l, w, base, name, ws)
+                e1.record(stream)
+                if it >= args.decode_warmup:
+                    per.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in per]))
+            kv_bytes = 2 * b * s * hkv * 128 * 2
+            scheds[name] = {"factor": jl.jl_schedule_factor(s, big_l, w, name), "prefill_ms": round(sp_ms, 4),
+                            "prefill_tflops": round(flops / (sp_ms * 1e-3) / 1e12, 2),
+                            "decode_us_median": round(us, 2), "decode_GB_s": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
+            log(f"schedule {name} (factor {scheds[name]['factor']:.4g}): prefill {sp_ms:.2f} ms "
+                f"({scheds[name]['prefill_tflops']} TFLOP/s), decode {us:.2f} us")
+        result["schedules"] = scheds
         del caches, slices
 
         # variable-length batched decode: 8 sequences of 16K..128K keys (g = 1..4 within one

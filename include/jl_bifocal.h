@@ -225,6 +225,62 @@ jl_status jl_plain_decode_varlen(const void* q, const void* k_cache, const void*
                                  int32_t head_dim, float softmax_scale, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ---- Long-range schedules -------------------------------------------------
+ * The long-range branch rescales positions by a factor that follows the current
+ * length, and the method is reported to be robust across rescaling schedules
+ * (seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap";
+ * news.transform-ai.online, "How Jet-Long works": the far window's frequencies
+ * are scaled from the current sequence length).  Three schedules, selected by
+ * `schedule`; the local branch keeps original positions in all of them, and a
+ * remote query at p and key at j are scored at positions a_q(p), a_k(j):
+ *   JL_SCHED_GROUPED    (0) a_q(p) = floor(p/g), a_k(j) = floor(j/g), g = jl_group_factor:
+ *                           what every other entry point computes.
+ *   JL_SCHED_SEAM       (1) a_q(p) = floor(p/g) + W - floor(W/g), a_k(j) = floor(j/g): the
+ *                           shift makes remote distances continue the local ones at the
+ *                           seam (distance W or W+1 at p - j = W); g is the smallest
+ *                           integer that keeps every shifted distance <= L-1.  Needs W < L.
+ *   JL_SCHED_FRACTIONAL (2) a_q(p) = p/l, a_k(j) = j/l with the real l = max(1, (s-1)/(L-1)):
+ *                           the remote branch is RoPE with theta/l.  Needs L >= 2 and
+ *                           s < 2^30.
+ * Every schedule is the base model when s <= L. */
+#define JL_SCHED_GROUPED    0
+#define JL_SCHED_SEAM       1
+#define JL_SCHED_FRACTIONAL 2
+
+/* The schedule's factor for a sequence of s keys: g for the two integer
+ * schedules, l for the fractional one; 0.0 for invalid arguments (s < 1,
+ * s > 2^31-1, L < 1, W < 1, W > L, or the schedule's own conditions above). */
+double jl_schedule_factor(int64_t seq_len, int64_t pretrained_window, int64_t local_window,
+                          int32_t schedule);
+
+/* Bifocal prefill under a long-range schedule.  Arguments, layouts and errors as
+ * jl_bifocal_prefill_ws, plus `schedule`; s = n_kv.  With a workspace (non-NULL,
+ * >= jl_bifocal_prefill_workspace_size bytes) the corrected keys are written
+ * there first and the attention kernel stages them (the two-launch form of
+ * jl_bifocal_prefill_ws); with workspace == NULL and workspace_bytes == 0 the
+ * keys are corrected tile by tile inside the attention kernel (the single-kernel
+ * form of jl_bifocal_prefill).  JL_SCHED_GROUPED gives bitwise the result of
+ * those two entry points. */
+jl_status jl_bifocal_prefill_sched(const void* q, const void* k, const void* v, void* out,
+                                   float* lse, int32_t batch, int32_t n_q, int32_t n_kv,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                   int64_t pretrained_window, int64_t local_window,
+                                   double rope_base, int32_t schedule, float softmax_scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bifocal decode under a long-range schedule.  seq_lens == NULL: every sequence
+ * holds n_kv keys (arguments as jl_bifocal_decode); otherwise sequence b holds
+ * seq_lens[b] keys of a cache of n_kv = max_seq_len positions (arguments as
+ * jl_bifocal_decode_varlen), the factor, the seam shift and the rate taken per
+ * sequence.  JL_SCHED_GROUPED gives bitwise the result of jl_bifocal_decode
+ * (seq_lens NULL) or jl_bifocal_decode_varlen. */
+jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void* v_cache,
+                                  void* out, float* lse, const int32_t* seq_lens, int32_t batch,
+                                  int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int64_t pretrained_window, int64_t local_window,
+                                  double rope_base, int32_t schedule, float softmax_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

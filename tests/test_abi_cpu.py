@@ -218,3 +218,61 @@ def test_error_message_cleared_on_success_path_is_thread_local(lib):
     t.start()
     t.join()
     assert msg and other == [b""]
+
+
+def test_schedule_factor_matches_oracle(lib):
+    # the library's factor search (host side of the same function the decode
+    # kernel runs per sequence) against the oracle's direct searches
+    for s in list(range(1, 130)) + [257, 1000, 4097, 65537, 131072, 131073]:
+        for big_l in (2, 3, 8, 16, 33, 128, 32768):
+            for w in (1, 2, 7, 15, 32, 100, 4096):
+                if w > big_l:
+                    continue
+                assert lib.jl_schedule_factor(s, big_l, w, 0) == oracle.group_factor(s, big_l)
+                if w < big_l:
+                    assert lib.jl_schedule_factor(s, big_l, w, 1) == oracle.seam_group_factor(s, big_l, w), (s, big_l, w)
+                assert lib.jl_schedule_factor(s, big_l, w, 2) == oracle.fractional_factor(s, big_l)
+    assert lib.jl_schedule_factor(100, 16, 16, 1) == 0.0      # seam needs W < L
+    assert lib.jl_schedule_factor(100, 1, 1, 2) == 0.0        # fractional needs L >= 2
+    assert lib.jl_schedule_factor(100, 16, 4, 3) == 0.0       # unknown schedule
+    assert lib.jl_schedule_factor(0, 16, 4, 0) == 0.0
+    assert jl.jl_schedule_factor(131072, 32768, 4096, "seam") == 5.0
+
+
+def test_schedule_entry_points_validation(lib):
+    def pre(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, batch=1, n_q=64, n_kv=64, hq=4, hkv=2, d=128, L=16, w=8,
+                 base=1e4, sched=1, scale=0.0, ws=None, wsb=0)
+        a.update(kw)
+        return lib.jl_bifocal_prefill_sched(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["n_q"],
+                                            a["n_kv"], a["hq"], a["hkv"], a["d"], a["L"], a["w"], a["base"],
+                                            a["sched"], a["scale"], a["ws"], a["wsb"], None)
+
+    need = lib.jl_bifocal_decode_workspace_size(1, 100, 4, 2, 128)
+
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, sl=None, batch=1, n_kv=100, hq=4, hkv=2, d=128, L=16,
+                 w=8, base=1e4, sched=2, scale=0.0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_bifocal_decode_sched(a["q"], a["k"], a["v"], a["out"], a["lse"], a["sl"], a["batch"],
+                                           a["n_kv"], a["hq"], a["hkv"], a["d"], a["L"], a["w"], a["base"],
+                                           a["sched"], a["scale"], a["ws"], a["wsb"], None)
+
+    pre_need = lib.jl_bifocal_prefill_workspace_size(1, 64, 2, 128)
+    for call in (pre, dec):
+        assert call(sched=3) == INVALID
+        assert call(sched=-1) == INVALID
+        assert call(sched=1, w=16) == INVALID             # seam needs W < L
+        assert call(sched=2, L=1, w=1) == INVALID         # fractional needs L >= 2
+        assert call(w=17) == INVALID                      # W > L
+        assert call(d=64) == UNSUPPORTED
+        if not _has_gpu():
+            for sched in (0, 1, 2):
+                assert call(sched=sched) == DEVICE
+    assert pre(ws=FAKE, wsb=pre_need - 1) == WORKSPACE     # a workspace selects the two-launch form
+    assert pre(ws=None, wsb=pre_need) == INVALID           # bytes without a pointer
+    assert dec(sl=FAKE + 2) == INVALID                     # misaligned seq_lens
+    assert dec(wsb=need - 1) == WORKSPACE
+    if not _has_gpu():
+        assert pre(ws=FAKE, wsb=pre_need) == DEVICE
+        assert dec(sl=FAKE) == DEVICE

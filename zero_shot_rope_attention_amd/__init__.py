@@ -31,6 +31,10 @@ __all__ = [
     "jl_plain_decode_varlen",
     "jl_sliding_prefill",
     "jl_sliding_decode",
+    "SCHEDULES",
+    "jl_schedule_factor",
+    "jl_bifocal_prefill_sched",
+    "jl_bifocal_decode_sched",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
@@ -60,6 +64,11 @@ _SIGNATURES = {
                                       _vp]),
     "jl_sliding_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
     "jl_sliding_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]),
+    "jl_schedule_factor": (ctypes.c_double, [_i64, _i64, _i64, _i32]),
+    "jl_bifocal_prefill_sched": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                        _f64, _i32, _f32, _vp, _sz, _vp]),
+    "jl_bifocal_decode_sched": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                       _f64, _i32, _f32, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -231,3 +240,47 @@ def jl_sliding_decode(q, k_cache, v_cache, out, lse, local_window, workspace, so
     _check(load_library().jl_sliding_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b, n_kv, hq,
                                             hkv, d, int(local_window), float(softmax_scale), _ptr(workspace), nbytes,
                                             _stream(stream)))
+
+
+# Long-range schedules, numbered as in the C header (JL_SCHED_*).
+SCHEDULES = {"grouped": 0, "seam": 1, "fractional": 2}
+
+
+def _schedule_id(schedule) -> int:
+    if isinstance(schedule, str):
+        if schedule not in SCHEDULES:
+            raise ValueError(f"unknown schedule {schedule!r}")
+        return SCHEDULES[schedule]
+    return int(schedule)
+
+
+def jl_schedule_factor(seq_len, pretrained_window, local_window, schedule="grouped") -> float:
+    """g (integer schedules) or l (fractional) for a sequence of seq_len keys; 0.0 if invalid."""
+    return float(load_library().jl_schedule_factor(int(seq_len), int(pretrained_window), int(local_window),
+                                                   _schedule_id(schedule)))
+
+
+def jl_bifocal_prefill_sched(q, k, v, out, lse, pretrained_window, local_window, rope_base, schedule,
+                             workspace=None, softmax_scale=0.0, stream=None):
+    """Bifocal prefill under a long-range schedule ("grouped", "seam", "fractional");
+    with a workspace the two-launch form, without one the single kernel."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_prefill_sched(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq, hkv, d, int(pretrained_window),
+        int(local_window), float(rope_base), _schedule_id(schedule), float(softmax_scale), _ptr(workspace), nbytes,
+        _stream(stream)))
+
+
+def jl_bifocal_decode_sched(q, k_cache, v_cache, out, lse, seq_lens, pretrained_window, local_window, rope_base,
+                            schedule, workspace, softmax_scale=0.0, stream=None):
+    """Bifocal decode under a long-range schedule; seq_lens None (every sequence
+    holds the whole cache) or an int32 device tensor [B]."""
+    b, _, hq, d = q.shape
+    n_kv, hkv = k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_decode_sched(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _seq_lens_ptr(seq_lens), b, n_kv, hq, hkv, d,
+        int(pretrained_window), int(local_window), float(rope_base), _schedule_id(schedule), float(softmax_scale),
+        _ptr(workspace), nbytes, _stream(stream)))

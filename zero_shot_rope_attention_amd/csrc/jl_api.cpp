@@ -337,4 +337,89 @@ jl_status jl_bifocal_decode_varlen(const void* q, const void* k_cache, const voi
   return launched(jl::launch_decode(true, p, static_cast<hipStream_t>(stream)));
 }
 
+static_assert(JL_SCHED_GROUPED == jl::kSchedGrouped && JL_SCHED_SEAM == jl::kSchedSeam &&
+                  JL_SCHED_FRACTIONAL == jl::kSchedFractional,
+              "schedule numbers of the C ABI and the kernels");
+
+static jl_status check_schedule(int32_t schedule, int64_t big_l, int64_t w, int64_t n_kv) {
+  if (schedule == jl::kSchedGrouped) return JL_OK;
+  if (schedule == jl::kSchedSeam) {
+    if (w >= big_l)
+      return fail(JL_ERR_INVALID_ARG, "the seam-shifted schedule needs local_window (%lld) < pretrained_window (%lld)",
+                  (long long)w, (long long)big_l);
+    return JL_OK;
+  }
+  if (schedule == jl::kSchedFractional) {
+    if (big_l < 2) return fail(JL_ERR_INVALID_ARG, "the fractional schedule needs pretrained_window >= 2");
+    if (n_kv >= jl::kFracGroup)
+      return fail(JL_ERR_UNSUPPORTED, "the fractional schedule supports at most %d keys", jl::kFracGroup - 1);
+    return JL_OK;
+  }
+  return fail(JL_ERR_INVALID_ARG, "unknown schedule %d", (int)schedule);
+}
+
+double jl_schedule_factor(int64_t seq_len, int64_t pretrained_window, int64_t local_window, int32_t schedule) {
+  if (seq_len < 1 || seq_len > 0x7fffffff || pretrained_window < 1 || local_window < 1 ||
+      local_window > pretrained_window)
+    return 0.0;
+  if (check_schedule(schedule, pretrained_window, local_window, seq_len) != JL_OK) return 0.0;
+  if (schedule == jl::kSchedFractional)
+    return seq_len <= pretrained_window ? 1.0 : (double)(seq_len - 1) / (double)(pretrained_window - 1);
+  const int32_t w = (int32_t)(local_window < seq_len ? local_window : seq_len);
+  return (double)jl::sched_group((int32_t)seq_len, pretrained_window, w, schedule);
+}
+
+jl_status jl_bifocal_prefill_sched(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
+                                   int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int64_t pretrained_window, int64_t local_window,
+                                   double rope_base, int32_t schedule, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(check_schedule(schedule, pretrained_window, local_window, n_kv));
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  const int32_t g = jl::sched_group(n_kv, pretrained_window, w, schedule);
+  // a workspace selects the two-launch form (corrected keys written first); none, the single kernel
+  const bool two_launch = workspace != nullptr || workspace_bytes != 0;
+  if (g > 1 && two_launch) {
+    JL_TRY(check_pointer(workspace, "workspace"));
+    const size_t need = jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim);
+    if (workspace_bytes < need)
+      return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  }
+  JL_TRY(device_check());
+  const jl::PrefillMode mode = g == 1 ? jl::kModePlain : (two_launch ? jl::kModeBifocalPre : jl::kModeBifocal);
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, mode == jl::kModeBifocalPre ? workspace : nullptr, batch,
+                       n_q, n_kv, n_q_heads, n_kv_heads, g, w, rope_base, scale};
+  p.q_shift = jl::sched_q_shift(g, w, schedule);
+  p.rate = jl::sched_rate(n_kv, pretrained_window, schedule);
+  return launched(jl::launch_prefill(mode, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                  const int32_t* seq_lens, int32_t batch, int32_t n_kv, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                  int64_t local_window, double rope_base, int32_t schedule, float softmax_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_cache, v_cache, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  if (seq_lens) JL_TRY(check_seq_lens(seq_lens));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(check_schedule(schedule, pretrained_window, local_window, n_kv));
+  JL_TRY(device_check());
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  // uniform lengths with g = 1 run the plain kernel; otherwise g, the shift and the
+  // rate are taken per sequence in the kernels
+  const bool bif = seq_lens != nullptr || jl::sched_group(n_kv, pretrained_window, w, schedule) > 1;
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, seq_lens, batch, n_kv, n_q_heads, n_kv_heads, pretrained_window,
+                      w, rope_base, scale, workspace};
+  p.schedule = schedule;
+  return launched(jl::launch_decode(bif, p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

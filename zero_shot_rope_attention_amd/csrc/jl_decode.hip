@@ -56,13 +56,13 @@ struct DecodeArgs {
   int32_t kpw;         // keys per wave = 32 nb; a chunk is kWaves * kpw keys
   int32_t order_ncu;   // > 0: workgroup order interleaves heads with this stride (the CU count); 0: chunk-major
   int32_t sliding;     // 1: sliding window, only the newest min(W, s) keys (plain kernel)
+  int32_t sched;       // long-range schedule (Schedule), per sequence
   float scale_log2;
-  float theta_rev32[kHalfD];
   double theta_rev[kHalfD];
 };
 
-// How one sequence of s keys is cut: g = g(s) for the bifocal kernel (1 for
-// plain); with g > 1 the remote prefix [0, s - min(W, s)) is cut into n_rem
+// How one sequence of s keys is cut: g = g(s) of the schedule for the bifocal
+// kernel (1 for plain); with g > 1 the remote prefix [0, s - min(W, s)) is cut into n_rem
 // chunks of kpg keys and the local suffix into the rest, so that no chunk
 // straddles the boundary; with g = 1 every chunk is local (base scores).
 // A sliding window (plain attention over the newest min(W, s) keys) has no
@@ -70,9 +70,10 @@ struct DecodeArgs {
 struct SeqSplit {
   int g, remote_end, n_rem, n_chunks;
 };
-__device__ __forceinline__ SeqSplit seq_split(int s, bool bif, int64_t big_l, int w_req, int kpg, bool sliding) {
+__device__ __forceinline__ SeqSplit seq_split(int s, bool bif, int64_t big_l, int w_req, int kpg, bool sliding,
+                                              int sched) {
   SeqSplit r;
-  r.g = bif ? (int)((int64_t)(s - 1) / big_l + 1) : 1;  // smallest g with floor((s-1)/g) <= L-1
+  r.g = bif ? sched_group(s, big_l, w_req, sched) : 1;
   const int w = min(w_req, s);
   r.remote_end = (r.g > 1 || sliding) ? s - w : 0;
   r.n_rem = sliding ? 0 : (r.remote_end + kpg - 1) / kpg;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(16))) uint8_t s_v0[kWaves][kVBlockBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_v1[kWaves][kVBlockBytes];
   __shared__ float s_fb[kWaves][kHalfD];  // per wave: (c(ws) - c(p)) theta_d / (2 pi), reduced to [-1/2, 1/2]
-  __shared__ float s_th[kWaves][kHalfD];  // theta_d / (2 pi)
+  __shared__ float s_th[kWaves][kHalfD];  // theta_d / (2 pi) times the schedule's rate
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][kMaxGroup];
 
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int kpg = kWaves * a.kpw;
   const int s_len = seq_length(a.seq_lens, b, a.n_kv);
-  const SeqSplit sq = seq_split(s_len, BIF, a.pretrained_window, a.local_window, kpg, a.sliding != 0);
+  const SeqSplit sq = seq_split(s_len, BIF, a.pretrained_window, a.local_window, kpg, a.sliding != 0, a.sched);
   if (sp >= sq.n_chunks) return;  // a shorter sequence of the batch: no chunk here
   int ks, ke;
   bool remote = false;
@@ -217,11 +218,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // query fragment first (tiny), then the first two key/value blocks, so that
   // waiting for the former never waits for the stream.
   double th64 = 0.0;
-  float th32 = 0.0f;
-  if (BIF) {  // unconditional within the instantiation: keeps the wait for them exact
-    th64 = a.theta_rev[lane];
-    th32 = a.theta_rev32[lane];
-  }
+  if (BIF) th64 = a.theta_rev[lane];  // unconditional within the instantiation: keeps the wait for it exact
   const bool col_ok = n < a.grp;
   const uint16_t* qrow = a.q + ((int64_t)b * a.hq + kvh * a.grp + (col_ok ? n : 0)) * kD;
   u32x4 qraw[8];
@@ -242,10 +239,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(qraw[kk]);
 
   // Remote keys.  Rotations in the same planes commute and are orthogonal, so
-  // the grouped score rot(q, c(p) theta) . rot(k_j, c(j) theta) equals
-  // q . rot(k_j, (c(j) - c(p)) theta): only the key turns, by
-  //   (c(j) - c(p)) theta_d = (c(ws) - c(p)) theta_d - u(j) theta_d,
-  //   u = t - floor((r + t)/g), t = j - ws, r = ws mod g.
+  // the grouped score rot(q, c_q(p) theta) . rot(k_j, c(j) theta) equals
+  // q . rot(k_j, (c(j) - c_q(p)) theta): only the key turns, by
+  //   (c(j) - c_q(p)) theta_d = (c(ws) - c_q(p)) theta_d - u(j) theta_d,
+  //   u = t - floor((r + t)/g), t = j - ws, r = ws mod g,
+  // with c(j) = floor(j/g) - j, c_q(p) = c(p) + the schedule's query shift, and
+  // theta times the schedule's rate (fractional: g = 2^30 makes u = t).
   // The wave's part is reduced in fp64 once; the per-key part u theta_d
   // (u < 512, the longest wave) is exact enough in fp32, and the sum (below 82 revolutions) lies
   // inside the domain of the hardware sine and cosine, which reduce it exactly.
@@ -253,11 +252,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const float inv_g = 1.0f / (float)sq.g;
   if (BIF && remote) {
     const int p = s_len - 1;  // the query's position
-    const long long cb = ((long long)(ws / sq.g) - ws) - ((long long)(p / sq.g) - p);
+    const long long cq = (long long)(p / sq.g) - p + sched_q_shift(sq.g, a.local_window, a.sched);
+    const long long cb = ((long long)(ws / sq.g) - ws) - cq;
     r_s = ws % sq.g;
-    const double r = (double)cb * th64;
+    const double th = th64 * sched_rate(s_len, a.pretrained_window, a.sched);
+    const double r = (double)cb * th;
     s_fb[wave][lane] = (float)(r - __builtin_rint(r));
-    s_th[wave][lane] = th32;
+    s_th[wave][lane] = (float)th;
     __builtin_amdgcn_wave_barrier();
   }
 
@@ -436,7 +437,7 @@ struct CombineArgs {
   uint16_t* out;
   float* lse;
   const int32_t* seq_lens;
-  int32_t n_kv, hq, n_wg, local_window, kpg, bif, sliding;
+  int32_t n_kv, hq, n_wg, local_window, kpg, bif, sliding, sched;
   int64_t pretrained_window;
 };
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const CombineArgs ca) {
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const C
   const int tid = threadIdx.x;
   const int cl = tid >> 5, c4 = tid & 31;
   const int n_wg = seq_split(seq_length(ca.seq_lens, (int)(bh / ca.hq), ca.n_kv), ca.bif != 0, ca.pretrained_window,
-                             ca.local_window, ca.kpg, ca.sliding != 0).n_chunks;
+                             ca.local_window, ca.kpg, ca.sliding != 0, ca.sched).n_chunks;
   const float* pl = ca.part_lse + bh * ca.n_wg;  // rows of ca.n_wg slots, the first n_wg filled
   const float* po = ca.part_o + bh * ca.n_wg * kD + 4 * c4;
   uint16_t* out = ca.out;
@@ -573,6 +574,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   if (p.sliding && bifocal) return hipErrorInvalidValue;
   a.pretrained_window = bifocal ? p.pretrained_window : 1;
   a.local_window = (bifocal || p.sliding) ? p.local_window : 0;
+  a.sched = bifocal ? p.schedule : kSchedGrouped;
   a.nb = decode_blocks_per_wave(p.batch, p.n_kv, p.n_kv_heads);
   if (p.sliding) {
     // chunks sized for the window's keys, if their count fits the workspace bound
@@ -590,7 +592,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
     a.n_wg = (w + chunk - 1) / chunk;
   } else {
     // every sequence holds n_kv keys: exactly its chunks (the kernels' cut, on the host)
-    const int64_t g = bifocal ? (int64_t)(p.n_kv - 1) / p.pretrained_window + 1 : 1;
+    const int32_t g = bifocal ? sched_group(p.n_kv, a.pretrained_window, a.local_window, a.sched) : 1;
     const int32_t remote_end = g > 1 ? p.n_kv - (p.local_window < p.n_kv ? p.local_window : p.n_kv) : 0;
     const int32_t n_rem = (remote_end + chunk - 1) / chunk;
     a.n_wg = n_rem + (p.n_kv - remote_end + chunk - 1) / chunk;
@@ -604,10 +606,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
     for (int d = 0; d < kHalfD; ++d) cached_rev[d] = std::pow(p.rope_base, -2.0 * d / kD) / two_pi;
     cached_base = p.rope_base;
   }
-  for (int d = 0; d < kHalfD; ++d) {
-    a.theta_rev[d] = cached_rev[d];
-    a.theta_rev32[d] = (float)cached_rev[d];
-  }
+  for (int d = 0; d < kHalfD; ++d) a.theta_rev[d] = cached_rev[d];
   const size_t rows = (size_t)p.batch * p.n_q_heads * decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);
   a.part_o = static_cast<float*>(p.workspace);
   a.part_lse = a.part_o + rows * kD;
@@ -638,6 +637,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   ca.kpg = chunk;
   ca.bif = bifocal ? 1 : 0;
   ca.sliding = a.sliding;
+  ca.sched = a.sched;
   ca.pretrained_window = a.pretrained_window;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kCombineThreads), 0, stream, ca);
   return hipGetLastError();

@@ -12,6 +12,50 @@ namespace jl {
 // workspace (one elementwise pass) and stages them like plain keys.
 enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2, kModeBifocalPre = 3, kModeSliding = 4 };
 
+// Long-range schedules: where a remote query at p and a remote key at j are
+// moved before their score is taken (positions a_q(p), a_k(j)).
+//  kSchedGrouped:    a_q(p) = floor(p/g), a_k(j) = floor(j/g), g the smallest
+//                    integer with floor((s-1)/g) <= L-1.
+//  kSchedSeam:       a_q(p) = floor(p/g) + W - floor(W/g), a_k(j) = floor(j/g):
+//                    remote distances continue the local ones at the seam; g the
+//                    smallest integer keeping every shifted distance <= L-1.
+//  kSchedFractional: a_q(p) = p/l, a_k(j) = j/l, l = max(1, (s-1)/(L-1)).
+// The kernels see every schedule as integer grouping: a group factor g, a query
+// shift, and a rate multiplying theta.  The fractional schedule is g = 2^30
+// (floor(p/g) = 0 for every position, so c(p) = -p) with rate 1 - 1/l: the
+// correction rot(x_p, -p (1 - 1/l) theta) moves x_p from p to p/l.
+enum Schedule : int32_t { kSchedGrouped = 0, kSchedSeam = 1, kSchedFractional = 2 };
+constexpr int32_t kFracGroup = 1 << 30;  // positions must stay below it
+
+// Group factor of a sequence of s >= 1 keys (1: the base model, no remote key
+// is moved).  Seam needs w < big_l whenever s > big_l.
+__host__ __device__ inline int32_t sched_group(int32_t s, int64_t big_l, int32_t w, int32_t sched) {
+  if ((int64_t)s <= big_l) return 1;
+  const int32_t l32 = (int32_t)big_l;  // big_l < s here
+  if (sched == kSchedFractional) return kFracGroup;
+  if (sched != kSchedSeam) return (s - 1) / l32 + 1;
+  // smallest g with floor((s-1)/g) - floor(w/g) <= r, r = L-1-w.  Since
+  // floor(D/g) <= floor((s-1)/g) - floor(w/g) <= floor(D/g) + 1 with D = s-1-w,
+  // no g <= D/(r+1) qualifies, and g = D/r + 1 (r >= 1) or g = s (r = 0) does:
+  // the search starts at the lower bound and takes few steps unless r is small.
+  const int32_t d = s - 1 - w, r = l32 - 1 - w;
+  if (d < 0) return 1;
+  int32_t g = d / (r + 1) + 1;
+  while (g < s && (s - 1) / g - w / g > r) ++g;  // g = s always qualifies when r >= 0
+  return g;
+}
+
+__host__ __device__ inline int32_t sched_q_shift(int32_t g, int32_t w, int32_t sched) {
+  return (sched == kSchedSeam && g > 1) ? w - w / g : 0;
+}
+
+// Factor on theta for the corrections: 1 - 1/l = (s - L)/(s - 1) for the
+// fractional schedule at s > L, else 1.
+__host__ __device__ inline double sched_rate(int32_t s, int64_t big_l, int32_t sched) {
+  if (sched != kSchedFractional || (int64_t)s <= big_l) return 1.0;
+  return (double)((int64_t)s - big_l) / (double)(s - 1);
+}
+
 // Everything a prefill launch needs; validated by the caller.
 struct PrefillProblem {
   const void* q;
@@ -27,6 +71,8 @@ struct PrefillProblem {
   int32_t local_window;  // W, already clamped to <= n_kv
   double rope_base;
   float softmax_scale;   // > 0
+  int32_t q_shift = 0;   // added to c(p) of the queries (seam schedule)
+  double rate = 1.0;     // factor on theta for the corrections (fractional schedule)
 };
 
 hipError_t launch_prefill(PrefillMode mode, const PrefillProblem& p, hipStream_t stream);
@@ -45,6 +91,7 @@ struct DecodeProblem {
   float softmax_scale;
   void* workspace;
   bool sliding = false;  // plain attention over the newest min(W, s) keys only (bifocal must be false)
+  int32_t schedule = kSchedGrouped;  // long-range schedule, taken per sequence in the kernels
 };
 
 // Number of key chunks the decode splits a cache of n_kv keys into (upper bound

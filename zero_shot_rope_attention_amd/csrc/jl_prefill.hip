@@ -54,6 +54,7 @@ struct PrefillArgs {
   int32_t n_units;    // batch * Hkv * (grp / hpw)
   int32_t g;          // group factor g(s)
   int32_t w;          // local window
+  int32_t q_shift;    // added to c(p) of the queries: the seam shift W - floor(W/g), else 0
   float inv_g;
   float scale_log2;   // softmax scale * log2(e)
   double theta_rev[kHalfD];  // theta_d / (2 pi)
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
     }
     if constexpr (kGrouped) {
       // q^g = rot(q, c(p) theta), rounded to bf16
-      const long long cq = row_ok ? (long long)(my_p / a.g) - my_p : 0;
+      const long long cq = row_ok ? (long long)(my_p / a.g) - my_p + a.q_shift : 0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         u32x4 lo, hi;
@@ -899,7 +900,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       qf[kk] = as_bf16x8(raw[kk]);
     }
     if constexpr (kGrouped) {
-      const long long cq = row_ok ? (long long)(my_p / a.g) - my_p : 0;
+      const long long cq = row_ok ? (long long)(my_p / a.g) - my_p + a.q_shift : 0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         u32x4 lo, hi;
@@ -1180,10 +1181,12 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   a.n_units = p.batch * p.n_kv_heads * (a.grp / hpw);
   a.g = p.group;
   a.w = p.local_window;
+  a.q_shift = p.q_shift;
   a.inv_g = 1.0f / (float)p.group;
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  // theta_d / (2 pi), times the schedule's rate (1 but for the fractional one)
   const double two_pi = 6.283185307179586476925286766559;
-  for (int d = 0; d < kHalfD; ++d) a.theta_rev[d] = std::pow(p.rope_base, -2.0 * d / kD) / two_pi;
+  for (int d = 0; d < kHalfD; ++d) a.theta_rev[d] = std::pow(p.rope_base, -2.0 * d / kD) / two_pi * p.rate;
   const long long blocks = (long long)a.n_units * a.n_qblocks;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
