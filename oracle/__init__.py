@@ -23,7 +23,12 @@ cited by page and section:
   long-range factor is computed from the current sequence length s; the merge
   combines the branches without double-counting.
 
-Parity status of each function is listed in ``oracle.bifocal``'s module docstring.
+* seventnews.com, "Empirical results that challenge the status quo": the method
+  runs inside Qwen3 models (1.7B, 4B, 8B) at up to 128K; ``oracle.layer`` states
+  one attention layer of them.
+
+Parity status of each function is listed in the module docstrings of
+``oracle.bifocal`` and ``oracle.layer``.
 """
 
 from .bifocal import (  # noqa: F401
@@ -47,3 +52,4 @@ from .bifocal import (  # noqa: F401
     long_range_schedule,
     merge_passes,
 )
+from .layer import qwen3_attention_layer, rms_norm_heads  # noqa: F401
