@@ -281,6 +281,57 @@ jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void
                                   double rope_base, int32_t schedule, float softmax_scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- A Qwen3-shaped attention layer ---------------------------------------
+ * The method runs inside Qwen3 models of 1.7B, 4B and 8B parameters at up to 128K
+ * tokens (seventnews.com, "Empirical results that challenge the status quo").
+ * One attention layer of such a model, with the attention step bifocal or plain,
+ * so that the attention's share of a layer can be measured:
+ *   1. qkv = x w_qkv^T (rocBLAS, bf16, fp32 accumulation), no bias;
+ *   2. per head: q = RMSNorm(q) * q_norm_weight, k = RMSNorm(k) * k_norm_weight
+ *      (RMSNorm(y) = y / sqrt(mean(y^2) + rms_eps), in fp32), both rotated by RoPE
+ *      at the tokens' positions p = n_kv - n_new + i; keys and values are written
+ *      to rows p of the caches (the cache keeps original positions: ResearchPod
+ *      transcript, cache exchange);
+ *   3. attention of the n_new queries over the n_kv cached keys: JL_LAYER_BIFOCAL
+ *      is jl_bifocal_prefill_sched in its two-launch form (n_new > 1) or
+ *      jl_bifocal_decode_sched (n_new == 1) under `schedule`; JL_LAYER_PLAIN is
+ *      plain causal attention (jl_plain_prefill / jl_plain_decode); scale 1/sqrt(128);
+ *   4. out = attn w_o^T (rocBLAS), no bias.
+ *   x             : bf16 [B, n_new, hidden]
+ *   w_qkv         : bf16 [(Hq + 2 Hkv) * 128, hidden]: the query heads' rows, then the
+ *                   key heads', then the value heads' (PyTorch Linear layout)
+ *   q/k_norm_weight: bf16 [128]
+ *   w_o           : bf16 [hidden, Hq * 128]
+ *   out           : bf16 [B, n_new, hidden]
+ *   k/v_cache     : bf16 [B, n_kv, Hkv, 128]; rows 0 .. n_kv-n_new-1 hold the earlier
+ *                   tokens (keys rotated at their positions) and are only read; rows
+ *                   n_kv-n_new .. n_kv-1 are written
+ *   workspace     : >= jl_qwen3_layer_workspace_size(...) bytes of device memory,
+ *                   16-byte aligned, contents ignored on entry
+ * All pointers are device pointers, 16-byte aligned, owned by the caller; the
+ * layer runs in stream order on `stream` and allocates nothing (rocBLAS keeps one
+ * handle per calling thread and device, created on first use).  Windows and
+ * schedule are checked as in jl_bifocal_prefill_sched when attention ==
+ * JL_LAYER_BIFOCAL and ignored otherwise (rope_base is always checked).
+ * Errors: JL_ERR_INVALID_ARG for bad pointers, sizes (n_new > n_kv, hidden < 1),
+ * rms_eps < 0 or an unknown attention kind; JL_ERR_UNSUPPORTED for head_dim != 128
+ * or sizes beyond 32-bit GEMM dimensions; JL_ERR_WORKSPACE; JL_ERR_DEVICE for
+ * launch or rocBLAS errors. */
+#define JL_LAYER_PLAIN   0
+#define JL_LAYER_BIFOCAL 1
+
+size_t jl_qwen3_layer_workspace_size(int32_t batch, int32_t n_new, int32_t n_kv, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim);
+
+jl_status jl_qwen3_attention_layer(const void* x, const void* w_qkv, const void* q_norm_weight,
+                                   const void* k_norm_weight, const void* w_o, void* out,
+                                   void* k_cache, void* v_cache, int32_t batch, int32_t n_new,
+                                   int32_t n_kv, int32_t hidden, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, float rms_eps,
+                                   int32_t attention, int64_t pretrained_window,
+                                   int64_t local_window, double rope_base, int32_t schedule,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,7 +61,7 @@ def _split_heads(qkv: np.ndarray, hq: int, hkv: int, d: int):
 
 def qwen3_attention_layer(x, w_qkv, gamma_q, gamma_k, w_o, n_q_heads, n_kv_heads, pretrained_window,
                           local_window, rope_base, past_k=None, past_v=None, eps=1e-6, bifocal=True,
-                          schedule="grouped", return_heads=False):
+                          schedule="grouped", return_heads=False, rows=None):
     """One attention layer over ``n_new`` new tokens appended to a cache.
 
     x        [B, n_new, H]                  hidden states of the new tokens
@@ -75,7 +75,9 @@ def qwen3_attention_layer(x, w_qkv, gamma_q, gamma_k, w_o, n_q_heads, n_kv_heads
     ``past + n_new`` rows; with ``return_heads`` also the normalised unrotated
     heads ``(q, k, v)`` and the attention output ``attn [B, n_new, Hq, D]``.
     Attention is ``oracle.bifocal.bifocal_three_pass`` under ``schedule`` (g from
-    s = past + n_new) when ``bifocal``, else plain causal attention.
+    s = past + n_new) when ``bifocal``, else plain causal attention.  ``rows``
+    selects new-token rows: ``out`` and ``attn`` then hold those rows only (the
+    caches are always whole).
     """
     x = np.asarray(x, dtype=np.float64)
     b, n_new, _ = x.shape
@@ -95,10 +97,10 @@ def qwen3_attention_layer(x, w_qkv, gamma_q, gamma_k, w_o, n_q_heads, n_kv_heads
     v_cache = v if past_v is None else np.concatenate([np.asarray(past_v, np.float64), v], axis=1)
     if bifocal:
         attn = _bf.bifocal_three_pass(q_rot, k_cache, v_cache, pretrained_window, local_window, rope_base,
-                                      schedule=schedule)["out"]
+                                      schedule=schedule, rows=rows)["out"]
     else:
-        attn = _bf.plain_causal_attention(q_rot, k_cache, v_cache)[0]
-    out = attn.reshape(b, n_new, hq * d) @ np.asarray(w_o, dtype=np.float64).T
+        attn = _bf.plain_causal_attention(q_rot, k_cache, v_cache, rows=rows)[0]
+    out = attn.reshape(b, attn.shape[1], hq * d) @ np.asarray(w_o, dtype=np.float64).T
     if return_heads:
         return out, k_cache, v_cache, (q, k, v), attn
     return out, k_cache, v_cache

@@ -4,7 +4,7 @@ bf16 inputs with fp32 accumulation).
 
 The same bar applies to the natural-log normaliser (lse).  Its error is set by
 the scores: the corrected vectors q^g and k^g are rounded to bf16 before the
-MFMA (relative error up to 2^-9 per element), which moves a grouped score
+MFMA (relative error up to 2^-8 per element, bf16's unit roundoff), which moves a grouped score
 tau * q^g . k^g by ~2e-3 RMS for N(0,1) inputs at D = 128, and the lse of a short
 row inherits that directly."""
 

@@ -276,3 +276,45 @@ def test_schedule_entry_points_validation(lib):
     if not _has_gpu():
         assert pre(ws=FAKE, wsb=pre_need) == DEVICE
         assert dec(sl=FAKE) == DEVICE
+
+
+def test_layer_workspace_and_validation(lib):
+    # projected q/k/v + rotated q + attention output (256-byte aligned regions), then the
+    # attention's workspace: corrected keys for a prefill, the decode partials for one token
+    t, hq, hkv = 2 * 100, 8, 2
+    up = lambda x: (x + 255) // 256 * 256
+    pre = up(t * (hq + 2 * hkv) * 256) + 2 * up(t * hq * 256) + up(2 * 300 * hkv * 256)
+    assert lib.jl_qwen3_layer_workspace_size(2, 100, 300, hq, hkv, 128) == pre
+    dec = up(2 * (hq + 2 * hkv) * 256) + 2 * up(2 * hq * 256) + up(lib.jl_bifocal_decode_workspace_size(2, 300, hq,
+                                                                                                          hkv, 128))
+    assert lib.jl_qwen3_layer_workspace_size(2, 1, 300, hq, hkv, 128) == dec
+    assert lib.jl_qwen3_layer_workspace_size(2, 301, 300, hq, hkv, 128) == 0
+    assert lib.jl_qwen3_layer_workspace_size(2, 100, 300, hq, hkv, 64) == 0
+
+    need = lib.jl_qwen3_layer_workspace_size(1, 64, 64, 4, 2, 128)
+
+    def call(**kw):
+        a = dict(x=FAKE, wqkv=FAKE, gq=FAKE, gk=FAKE, wo=FAKE, out=FAKE, kc=FAKE, vc=FAKE, batch=1, n_new=64, n_kv=64,
+                 hidden=256, hq=4, hkv=2, d=128, eps=1e-6, attn=1, L=16, w=8, base=1e4, sched=0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_qwen3_attention_layer(a["x"], a["wqkv"], a["gq"], a["gk"], a["wo"], a["out"], a["kc"], a["vc"],
+                                            a["batch"], a["n_new"], a["n_kv"], a["hidden"], a["hq"], a["hkv"], a["d"],
+                                            a["eps"], a["attn"], a["L"], a["w"], a["base"], a["sched"], a["ws"],
+                                            a["wsb"], None)
+
+    assert call(x=None) == INVALID
+    assert call(gk=FAKE + 8) == INVALID
+    assert call(hidden=0) == INVALID
+    assert call(n_new=65) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(attn=2) == INVALID
+    assert call(w=17) == INVALID                 # bifocal: W > L
+    assert call(sched=1, w=16) == INVALID        # seam needs W < L
+    assert call(d=64) == UNSUPPORTED
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=None) == INVALID
+    if not _has_gpu():
+        assert call() == DEVICE
+        assert call(attn=0, w=17) == DEVICE      # windows are not checked for the plain layer
+        assert lib.jl_qwen3_layer_workspace_size(1, 1, 64, 4, 2, 128) <= need
+        assert call(n_new=1) == DEVICE           # one new token: the decode path

@@ -115,3 +115,14 @@ def test_layer_in_two_chunks_equals_one_call():
     out2, k2, v2 = ol.qwen3_attention_layer(x[:, 61:], w_qkv, gq, gk, w_o, hq, hkv, big_l, w, base, k1, v1)
     assert np.abs(out2 - full[:, 61:]).max() <= 1e-12
     assert np.abs(k2 - kf).max() <= 1e-12 and np.abs(v2 - vf).max() <= 1e-12
+
+
+def test_layer_row_subset_matches_full():
+    b, hidden, hq, hkv, big_l, w, base = 1, 64, 4, 2, 16, 5, 1e4
+    w_qkv, gq, gk, w_o = _weights(9, hidden, hq, hkv)
+    x = np.random.default_rng(10).standard_normal((b, 50, hidden))
+    rows = np.array([0, 4, 5, 17, 49])
+    for bif in (True, False):
+        full, _, _ = ol.qwen3_attention_layer(x, w_qkv, gq, gk, w_o, hq, hkv, big_l, w, base, bifocal=bif)
+        part, _, _ = ol.qwen3_attention_layer(x, w_qkv, gq, gk, w_o, hq, hkv, big_l, w, base, bifocal=bif, rows=rows)
+        assert np.abs(part - full[:, rows]).max() <= 1e-13

@@ -35,6 +35,8 @@ __all__ = [
     "jl_schedule_factor",
     "jl_bifocal_prefill_sched",
     "jl_bifocal_decode_sched",
+    "jl_qwen3_layer_workspace_size",
+    "jl_qwen3_attention_layer",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
@@ -69,6 +71,9 @@ _SIGNATURES = {
                                         _f64, _i32, _f32, _vp, _sz, _vp]),
     "jl_bifocal_decode_sched": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
                                        _f64, _i32, _f32, _vp, _sz, _vp]),
+    "jl_qwen3_layer_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "jl_qwen3_attention_layer": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _f32, _i32, _i64, _i64, _f64, _i32, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -284,3 +289,23 @@ def jl_bifocal_decode_sched(q, k_cache, v_cache, out, lse, seq_lens, pretrained_
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _seq_lens_ptr(seq_lens), b, n_kv, hq, hkv, d,
         int(pretrained_window), int(local_window), float(rope_base), _schedule_id(schedule), float(softmax_scale),
         _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_qwen3_layer_workspace_size(batch, n_new, n_kv, n_q_heads, n_kv_heads, head_dim=128) -> int:
+    return int(load_library().jl_qwen3_layer_workspace_size(batch, n_new, n_kv, n_q_heads, n_kv_heads, head_dim))
+
+
+def jl_qwen3_attention_layer(x, w_qkv, q_norm_weight, k_norm_weight, w_o, out, k_cache, v_cache, workspace,
+                             bifocal=True, pretrained_window=1, local_window=1, rope_base=1e6, schedule="grouped",
+                             rms_eps=1e-6, stream=None):
+    """One Qwen3-shaped attention layer over x [B, n_new, hidden], appending to the
+    caches [B, n_kv, Hkv, 128] at rows n_kv - n_new ..; out [B, n_new, hidden]."""
+    b, n_new, hidden = x.shape
+    n_kv, hkv, d = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+    hq = w_o.shape[1] // d
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_qwen3_attention_layer(
+        _ptr(x), _ptr(w_qkv), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(w_o), _ptr(out), _ptr(k_cache),
+        _ptr(v_cache), b, n_new, n_kv, hidden, hq, hkv, d, float(rms_eps), 1 if bifocal else 0,
+        int(pretrained_window), int(local_window), float(rope_base), _schedule_id(schedule), _ptr(workspace), nbytes,
+        _stream(stream)))

@@ -17,11 +17,15 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libjetlong.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["jl_api.cpp", "jl_prefill.hip", "jl_decode.hip"]
+SOURCES = ["jl_api.cpp", "jl_prefill.hip", "jl_decode.hip", "jl_layer.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code; plain fp32 is used instead.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+# rocBLAS serves the projections of the attention layer (plain library GEMMs).
+LINK_FLAGS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]
 
 
 def hipcc() -> str:
@@ -36,7 +40,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS,
-           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES] + LINK_FLAGS
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -422,4 +422,110 @@ jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void
   return launched(jl::launch_decode(bif, p, static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of the attention layer: projected q/k/v, rotated queries, the
+// attention output, and the attention's own workspace (corrected keys for the
+// prefill, chunk partials for the decode), each 256-byte aligned.
+struct LayerWorkspace {
+  size_t qkv, q, attn, attn_ws, total;
+};
+static bool layer_workspace(int32_t batch, int32_t n_new, int32_t n_kv, int32_t hq, int32_t hkv, LayerWorkspace* l) {
+  const int64_t e_qkv = elements(batch, n_new, (int64_t)hq + 2 * (int64_t)hkv);
+  const int64_t e_q = elements(batch, n_new, hq);
+  if (e_qkv < 0 || e_q < 0 || elements(batch, n_kv, hkv) < 0) return false;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  l->qkv = 0;
+  l->q = up((size_t)e_qkv * 2);
+  l->attn = l->q + up((size_t)e_q * 2);
+  l->attn_ws = l->attn + up((size_t)e_q * 2);
+  const size_t aw = n_new == 1 ? jl::decode_workspace_bytes(batch, n_kv, hq, hkv)
+                               : (size_t)elements(batch, n_kv, hkv) * 2;
+  l->total = l->attn_ws + up(aw);
+  return true;
+}
+
+size_t jl_qwen3_layer_workspace_size(int32_t batch, int32_t n_new, int32_t n_kv, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim) {
+  if (batch < 1 || n_new < 1 || n_kv < n_new || n_q_heads < 1 || n_kv_heads < 1 || head_dim != 128 ||
+      n_q_heads % n_kv_heads != 0)
+    return 0;
+  LayerWorkspace l;
+  return layer_workspace(batch, n_new, n_kv, n_q_heads, n_kv_heads, &l) ? l.total : 0;
+}
+
+jl_status jl_qwen3_attention_layer(const void* x, const void* w_qkv, const void* q_norm_weight,
+                                   const void* k_norm_weight, const void* w_o, void* out, void* k_cache,
+                                   void* v_cache, int32_t batch, int32_t n_new, int32_t n_kv, int32_t hidden,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float rms_eps,
+                                   int32_t attention, int64_t pretrained_window, int64_t local_window,
+                                   double rope_base, int32_t schedule, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  const Shape s{batch, n_new, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(check_pointer(x, "x"));
+  JL_TRY(check_pointer(w_qkv, "w_qkv"));
+  JL_TRY(check_pointer(q_norm_weight, "q_norm_weight"));
+  JL_TRY(check_pointer(k_norm_weight, "k_norm_weight"));
+  JL_TRY(check_pointer(w_o, "w_o"));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(k_cache, "k_cache"));
+  JL_TRY(check_pointer(v_cache, "v_cache"));
+  JL_TRY(check_shape(s));
+  if (hidden < 1) return fail(JL_ERR_INVALID_ARG, "hidden must be >= 1 (got %d)", hidden);
+  if (!(rms_eps >= 0.0f) || std::isinf(rms_eps)) return fail(JL_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (attention != JL_LAYER_PLAIN && attention != JL_LAYER_BIFOCAL)
+    return fail(JL_ERR_INVALID_ARG, "unknown attention kind %d", (int)attention);
+  const bool bif_req = attention == JL_LAYER_BIFOCAL;
+  if (bif_req) {
+    JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+    JL_TRY(check_schedule(schedule, pretrained_window, local_window, n_kv));
+  } else if (!(rope_base > 1.0) || !std::isfinite(rope_base)) {
+    return fail(JL_ERR_INVALID_ARG, "rope_base must be finite and > 1");
+  }
+  const int64_t t = (int64_t)batch * n_new;
+  const int64_t n_qkv = ((int64_t)n_q_heads + 2 * (int64_t)n_kv_heads) * 128;
+  if (t > 0x7fffffff || n_qkv > 0x7fffffff || (int64_t)n_q_heads * 128 > 0x7fffffff ||
+      elements(t, hidden, 1) < 0)
+    return fail(JL_ERR_UNSUPPORTED, "layer sizes exceed the 32-bit GEMM dimensions");
+  LayerWorkspace l;
+  if (!layer_workspace(batch, n_new, n_kv, n_q_heads, n_kv_heads, &l))
+    return fail(JL_ERR_UNSUPPORTED, "tensor sizes overflow 64-bit element offsets");
+  JL_TRY(check_pointer(workspace, "workspace"));
+  if (workspace_bytes < l.total)
+    return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, l.total);
+  JL_TRY(device_check());
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* qkv = ws + l.qkv;
+  void* q = ws + l.q;
+  void* attn = ws + l.attn;
+  void* attn_ws = ws + l.attn_ws;
+  const float scale = 1.0f / std::sqrt(128.0f);
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  const int32_t g = bif_req ? jl::sched_group(n_kv, pretrained_window, w, schedule) : 1;
+  const bool bif = bif_req && g > 1;
+
+  hipError_t e = jl::launch_gemm_xwt(x, w_qkv, qkv, t, n_qkv, hidden, st);
+  if (e != hipSuccess) return launched(e);
+  jl::NormRopeProblem nr{qkv, q_norm_weight, k_norm_weight, q, k_cache, v_cache, batch, n_new, n_kv, n_q_heads,
+                         n_kv_heads, rms_eps, rope_base};
+  e = jl::launch_norm_rope(nr, st);
+  if (e != hipSuccess) return launched(e);
+  if (n_new == 1) {
+    jl::DecodeProblem p{q, k_cache, v_cache, attn, nullptr, nullptr, batch, n_kv, n_q_heads, n_kv_heads,
+                        bif ? pretrained_window : 1, bif ? w : 0, rope_base, scale, attn_ws};
+    p.schedule = bif ? schedule : jl::kSchedGrouped;
+    e = jl::launch_decode(bif, p, st);
+  } else {
+    jl::PrefillProblem p{q, k_cache, v_cache, attn, nullptr, nullptr, nullptr, bif ? attn_ws : nullptr, batch,
+                         n_new, n_kv, n_q_heads, n_kv_heads, bif ? g : 1, bif ? w : 1, rope_base, scale};
+    if (bif) {
+      p.q_shift = jl::sched_q_shift(g, w, schedule);
+      p.rate = jl::sched_rate(n_kv, pretrained_window, schedule);
+    }
+    e = jl::launch_prefill(bif ? jl::kModeBifocalPre : jl::kModePlain, p, st);
+  }
+  if (e != hipSuccess) return launched(e);
+  return launched(jl::launch_gemm_xwt(attn, w_o, out, t, hidden, (int64_t)n_q_heads * 128, st));
+}
+
 }  // extern "C"

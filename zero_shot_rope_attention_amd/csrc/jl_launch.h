@@ -101,4 +101,23 @@ size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads, in
 
 hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t stream);
 
+// Per-head RMSNorm of the query and key heads, RoPE at the tokens' positions
+// n_kv - n_new + i, and the append of keys and values to the caches.
+struct NormRopeProblem {
+  const void* qkv;      // bf16 [B * n_new, (Hq + 2 Hkv) D]: query heads, then key heads, then value heads
+  const void* gamma_q;  // bf16 [D]
+  const void* gamma_k;  // bf16 [D]
+  void* q;              // bf16 [B * n_new, Hq, D]  normalised, rotated queries
+  void* k_cache;        // bf16 [B, n_kv, Hkv, D]   rows n_kv - n_new .. n_kv - 1 written
+  void* v_cache;        // bf16 [B, n_kv, Hkv, D]
+  int32_t batch, n_new, n_kv, n_q_heads, n_kv_heads;
+  float eps;
+  double rope_base;
+};
+hipError_t launch_norm_rope(const NormRopeProblem& p, hipStream_t stream);
+
+// Row-major y[m, n] = x[m, k] w[n, k]^T in bf16 with fp32 accumulation (rocBLAS).
+hipError_t launch_gemm_xwt(const void* x, const void* w, void* y, int64_t m, int64_t n, int64_t k,
+                           hipStream_t stream);
+
 }  // namespace jl

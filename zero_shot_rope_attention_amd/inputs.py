@@ -10,6 +10,10 @@ Recipe: ``numpy.random.default_rng([workload_id, tensor_id])`` with tensor_id
 0/1/2 for Q/K/V, ``standard_normal(shape, float32)`` -> bf16 RNE.  The vectors
 are taken *as* the cached, already position-rotated Q and K (rotating an
 isotropic Gaussian leaves its distribution unchanged).
+
+The attention layer's inputs (``make_layer``) use tensor ids 3..7: hidden states
+x ~ N(0, 1); projections with N(0, 1/fan_in) entries, so that the projected heads
+have unit variance; RMSNorm scales 1 + N(0, 1/16).
 """
 
 from __future__ import annotations
@@ -17,6 +21,7 @@ from __future__ import annotations
 import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_X, TENSOR_WQKV, TENSOR_WO, TENSOR_GQ, TENSOR_GK = 3, 4, 5, 6, 7
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -58,3 +63,18 @@ def make_qkv(workload_id: int, batch: int, n_q: int, n_kv: int, n_q_heads: int,
     k = normal_bf16(workload_id, TENSOR_K, (batch, n_kv, n_kv_heads, head_dim))
     v = normal_bf16(workload_id, TENSOR_V, (batch, n_kv, n_kv_heads, head_dim))
     return q, k, v
+
+
+def make_layer(workload_id: int, batch: int, n_new: int, hidden: int, n_q_heads: int, n_kv_heads: int,
+               head_dim: int = 128):
+    """Inputs of one attention layer as bf16 bit arrays: x [B, n_new, hidden],
+    w_qkv [(Hq + 2 Hkv) D, hidden], w_o [hidden, Hq D], gamma_q and gamma_k [D]."""
+    x = normal_bf16(workload_id, TENSOR_X, (batch, n_new, hidden))
+    w_qkv = normal_bf16(workload_id, TENSOR_WQKV, ((n_q_heads + 2 * n_kv_heads) * head_dim, hidden),
+                        1.0 / np.sqrt(hidden))
+    w_o = normal_bf16(workload_id, TENSOR_WO, (hidden, n_q_heads * head_dim), 1.0 / np.sqrt(n_q_heads * head_dim))
+    gammas = []
+    for tid in (TENSOR_GQ, TENSOR_GK):
+        z = np.random.default_rng([int(workload_id), tid]).standard_normal(head_dim, dtype=np.float32)
+        gammas.append(f32_to_bf16_bits(np.float32(1.0) + np.float32(0.25) * z))
+    return x, w_qkv, w_o, gammas[0], gammas[1]
