@@ -20,7 +20,9 @@ hold them) and its overhead vs the plain decode built the same way; the plain
 causal prefill for comparison; the sliding-window layers of hybrid models; a
 batch of 8 sequences of different lengths; the prefill and decode under each
 long-range schedule (integer grouping, seam-shifted grouping, fractional
-scaling); and the fp64 CPU oracle timed on a bounded sample of rows.
+scaling); one Qwen3-8B-shaped attention layer (projections, norm, RoPE,
+attention) with the bifocal and with plain attention; and the fp64 CPU oracle
+timed on a bounded sample of rows.
 """
 
 from __future__ import annotations
@@ -113,6 +115,86 @@ def cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, n_rows, seed=0):
             "sample": f"{n_rows} random query rows x {grp} query heads (KV head 0) of the workload, "
                       f"fp64 numpy three-pass oracle, {dt:.1f} s; rate = algorithmic flops of those rows / time",
             "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def bench_layer(jl, torch, s, hq, hkv, big_l, w, base, args, result):
+    """One Qwen3-8B-shaped attention layer (hidden 4096) at this length: prefill of the
+    whole prompt and one decode step, with the bifocal attention and with plain attention.
+    Hidden states and weights are seeded device normals (N(0, 1), N(0, 1/fan_in))."""
+    dev = torch.device("cuda:0")
+    hidden = 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * scale).to(torch.bfloat16)
+
+    x = randn(1, s, hidden)
+    w_qkv = randn((hq + 2 * hkv) * 128, hidden, scale=hidden ** -0.5)
+    w_o = randn(hidden, hq * 128, scale=(hq * 128) ** -0.5)
+    gq, gk = 1.0 + randn(128, scale=0.25).float(), 1.0 + randn(128, scale=0.25).float()
+    gq, gk = gq.to(torch.bfloat16), gk.to(torch.bfloat16)
+    kc = torch.empty((1, s, hkv, 128), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    out = torch.empty_like(x)
+    ws = torch.empty(jl.jl_qwen3_layer_workspace_size(1, s, s, hq, hkv), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"shape": {"hidden": hidden, "q_heads": hq, "kv_heads": hkv, "head_dim": 128, "seq_len": s},
+           "data": "seeded device normals; projections by rocBLAS"}
+
+    def prefill(bif):
+        jl.jl_qwen3_attention_layer(x, w_qkv, gq, gk, w_o, out, kc, vc, ws, bifocal=bif, pretrained_window=big_l,
+                                    local_window=w, rope_base=base)
+
+    pre = {}
+    for name, bif in (("bifocal", True), ("plain", False)):
+        prefill(bif)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            prefill(bif)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        pre[name] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    res["prefill"] = {"bifocal_ms": round(pre["bifocal"], 3), "plain_ms": round(pre["plain"], 3),
+                      "overhead_vs_plain": round(pre["bifocal"] / pre["plain"] - 1.0, 4)}
+    if "prefill_ms" in result and "plain_prefill" in result:
+        att_b, att_p = result["prefill_ms"]["avg"], result["plain_prefill"]["ms"]
+        res["prefill"]["attention_share"] = round(att_b / pre["bifocal"], 4)
+        res["prefill"]["outside_attention_ms"] = round(pre["plain"] - att_p, 3)
+    log(f"layer prefill (hidden {hidden}, {s} tokens): bifocal {pre['bifocal']:.2f} ms, plain {pre['plain']:.2f} ms")
+
+    # one decode step: the token at position s-1 against the cache the prefill wrote
+    x1 = x[:, -1:].contiguous()
+    out1 = torch.empty_like(x1)
+    ws1 = torch.empty(jl.jl_qwen3_layer_workspace_size(1, 1, s, hq, hkv), dtype=torch.uint8, device=dev)
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_a.record(stream)
+    torch.cuda._sleep(1_000_000)
+    e_b.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles = int(1_000_000 * 3.0 / max(e_a.elapsed_time(e_b), 1e-3))
+    per = {"bifocal": [], "plain": []}
+    for it in range(args.decode_warmup + args.decode_iters // 2):
+        if it % 10 == 0:
+            torch.cuda._sleep(spin_cycles)
+        for name in ("bifocal", "plain"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            jl.jl_qwen3_attention_layer(x1, w_qkv, gq, gk, w_o, out1, kc, vc, ws1, bifocal=name == "bifocal",
+                                        pretrained_window=big_l, local_window=w, rope_base=base)
+            e1.record(stream)
+            if it >= args.decode_warmup:
+                per[name].append((e0, e1))
+    torch.cuda.synchronize()
+    dec = {n: float(np.median([a.elapsed_time(b_) * 1e3 for a, b_ in lst])) for n, lst in per.items()}
+    res["decode"] = {"bifocal_us": round(dec["bifocal"], 2), "plain_us": round(dec["plain"], 2),
+                     "overhead_vs_plain": round(dec["bifocal"] / dec["plain"] - 1.0, 4),
+                     "timing": "HIP events per call, calls queued back to back behind a spin kernel; the "
+                               "layer's 80 MiB of weights may stay in the last-level cache between calls"}
+    log(f"layer decode step at {s}: bifocal {dec['bifocal']:.2f} us, plain {dec['plain']:.2f} us")
+    del x, out, kc, vc, ws, ws1
+    return res
 
 
 def main():
@@ -420,6 +502,9 @@ def main():
             log(f"decode varlen 8 x (16K..128K): bifocal {vl['bifocal']['us_median']} us ({vl['bifocal']['GB_s']} GB/s), "
                 f"plain {vl['plain']['us_median']} us, overhead {vl['overhead_vs_plain'] * 100:.2f}%")
             del kv_b, vv_b
+
+    if not args.no_extras and b == 1:
+        result["layer"] = bench_layer(jl, torch, s, hq, hkv, big_l, w, base, args, result)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
