@@ -45,6 +45,7 @@ from .bifocal import (  # noqa: F401
     bifocal_decode,
     bifocal_decode_varlen,
     plain_decode_varlen,
+    bifocal_prefill_varlen,
     sliding_window_attention,
     SCHEDULES,
     seam_group_factor,

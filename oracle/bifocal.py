@@ -33,6 +33,10 @@ Parity pins (see ``tests/test_oracle_*.py``):
   form equals the brute force under each schedule; every schedule recovers the
   base model when s <= L; the factors are minimal by exhaustive check (parity of
   the variants' readings themselves unpinned: the pages print no value for them).
+* ``bifocal_prefill_varlen``: each sequence's packed rows equal
+  ``bifocal_bruteforce`` on its own rows and prefix, with the cache rows past the
+  prefix set to NaN; a sequence with no new rows is skipped; with one sequence
+  it equals ``bifocal_three_pass``.
 * ``sliding_window_attention``: torch's fp64 ``scaled_dot_product_attention`` with an
   explicit band mask; equals pass A of ``bifocal_three_pass``; equals
   ``plain_causal_attention`` when the window covers every key; W = 1 returns v_p.
@@ -65,6 +69,7 @@ __all__ = [
     "bifocal_decode",
     "bifocal_decode_varlen",
     "plain_decode_varlen",
+    "bifocal_prefill_varlen",
     "sliding_window_attention",
     "SCHEDULES",
     "seam_group_factor",
@@ -572,6 +577,40 @@ def bifocal_decode_varlen(q, k_cache, v_cache, seq_lens, pretrained_window, loca
         outs.append(o)
         lses.append(l)
     return np.concatenate(outs, axis=0), np.concatenate(lses, axis=0)
+
+
+def bifocal_prefill_varlen(q, cu_seqlens_q, k_cache, v_cache, seq_lens, pretrained_window, local_window,
+                           rope_base, softmax_scale=None, schedule="grouped", bifocal=True):
+    """A batch of sequences of different lengths, each with its own chunk of new
+    queries against its own cache (the cache keeps original positions and the
+    factor follows each sequence's current length: ResearchPod transcript, cache
+    exchange; seventnews.com, "How bifocal attention sidesteps the fixed-scaling
+    trap").  Sequence b owns the packed query rows ``cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1`` of ``q [total_q, Hq, D]``, at positions ``s_b - n_b + i``
+    with ``s_b = seq_lens[b]`` keys in rows 0 .. s_b-1 of ``k_cache, v_cache [B, N,
+    Hkv, D]``.  Each sequence is exactly ``bifocal_three_pass`` (or plain causal
+    attention with ``bifocal=False``) on its own rows and prefix.
+    Returns ``(out [total_q, Hq, D], lse [Hq, total_q])``.
+    """
+    q = _as_f64(q)
+    cu = [int(x) for x in cu_seqlens_q]
+    hq, d = q.shape[1], q.shape[2]
+    out = np.zeros((q.shape[0], hq, d))
+    lse = np.zeros((hq, q.shape[0]))
+    for bi, s in enumerate(int(x) for x in seq_lens):
+        r0, r1 = cu[bi], cu[bi + 1]
+        if r1 == r0:
+            continue
+        kb, vb = k_cache[bi:bi + 1, :s], v_cache[bi:bi + 1, :s]
+        if bifocal:
+            r = bifocal_three_pass(q[None, r0:r1], kb, vb, pretrained_window, local_window, rope_base,
+                                   softmax_scale=softmax_scale, schedule=schedule)
+            o, l = r["out"], r["lse"]
+        else:
+            o, l = plain_causal_attention(q[None, r0:r1], kb, vb, softmax_scale=softmax_scale)
+        out[r0:r1] = o[0]
+        lse[:, r0:r1] = l[0]
+    return out, lse
 
 
 def plain_decode_varlen(q, k_cache, v_cache, seq_lens, softmax_scale=None):

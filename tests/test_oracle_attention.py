@@ -413,3 +413,43 @@ def test_fractional_two_dim_closed_form():
     k = np.array([[r_k[j] * math.cos(a_k[j] + j), r_k[j] * math.sin(a_k[j] + j)] for j in range(s)])
     r = oracle.bifocal_three_pass(q[None, :, None], k[None, :, None], v, big_l, w, 1e4, schedule="fractional")
     assert np.abs(r["out"][0, :, 0] - expected).max() <= 1e-12
+
+
+def test_prefill_varlen_equals_bruteforce_per_sequence():
+    # four sequences in one padded cache: (new rows, keys) = (20, 20), (7, 33), (0, 9),
+    # (1, 40) with L = 8, W = 3; rows past a prefix are NaN
+    big_l, w, base, d, hq, hkv = 8, 3, 1e4, 16, 4, 2
+    spec = [(20, 20), (7, 33), (0, 9), (1, 40)]
+    n_max = max(s for _, s in spec)
+    rng = np.random.default_rng(777)
+    cu = np.concatenate([[0], np.cumsum([n for n, _ in spec])])
+    q = np.zeros((cu[-1], hq, d))
+    k = np.full((len(spec), n_max, hkv, d), np.nan)
+    v = np.full((len(spec), n_max, hkv, d), np.nan)
+    raws = []
+    for bi, (n, s) in enumerate(spec):
+        q_raw = rng.standard_normal((1, n, hq, d))
+        k_raw = rng.standard_normal((1, s, hkv, d))
+        v_s = rng.standard_normal((1, s, hkv, d))
+        q_rot, k_rot = _prerotate(q_raw, k_raw, base)
+        q[cu[bi]:cu[bi + 1]], k[bi, :s], v[bi, :s] = q_rot[0], k_rot[0], v_s[0]
+        raws.append((q_raw, k_raw, v_s))
+    for sched in oracle.SCHEDULES:
+        out, lse = oracle.bifocal_prefill_varlen(q, cu, k, v, [s for _, s in spec], big_l, w, base, schedule=sched)
+        for bi, (n, s) in enumerate(spec):
+            if n == 0:
+                continue
+            o2, l2 = oracle.bifocal_bruteforce(*raws[bi], big_l, w, base, schedule=sched)
+            assert np.abs(out[cu[bi]:cu[bi + 1]] - o2[0]).max() <= 1e-12
+            assert np.abs(lse[:, cu[bi]:cu[bi + 1]] - l2[0]).max() <= 1e-11
+    # plain: torch's fp64 attention per sequence
+    out_p, _ = oracle.bifocal_prefill_varlen(q, cu, k, v, [s for _, s in spec], big_l, w, base, bifocal=False)
+    for bi, (n, s) in enumerate(spec):
+        if n == 0:
+            continue
+        qt = torch.from_numpy(q[cu[bi]:cu[bi + 1]][None]).permute(0, 2, 1, 3)
+        kt = torch.from_numpy(np.repeat(k[bi:bi + 1, :s], hq // hkv, axis=2)).permute(0, 2, 1, 3)
+        vt = torch.from_numpy(np.repeat(v[bi:bi + 1, :s], hq // hkv, axis=2)).permute(0, 2, 1, 3)
+        mask = torch.from_numpy(np.arange(s)[None, :] <= (s - n + np.arange(n))[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask).permute(0, 2, 1, 3)
+        assert np.abs(out_p[cu[bi]:cu[bi + 1]] - ref.numpy()[0]).max() <= 1e-12
