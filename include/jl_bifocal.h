@@ -281,6 +281,52 @@ jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void
                                   double rope_base, int32_t schedule, float softmax_scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Variable-length prefill batches ---------------------------------------
+ * A batch of sequences, each with its own chunk of new queries against its own
+ * cache: sequence b owns the packed query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * (n_b of them) at positions s_b - n_b + i, where s_b = seq_lens[b] keys sit in rows
+ * 0 .. s_b-1 of its cache, the new tokens' own keys included.  The cache keeps
+ * original positions and the factor follows each sequence's current length
+ * (ResearchPod transcript, cache exchange; seventnews.com, "How bifocal attention
+ * sidesteps the fixed-scaling trap"): g, the seam shift and the fractional rate
+ * are taken per sequence from s_b.
+ *   q, out        : bf16 [total_q, Hq, D], packed rows
+ *   k/v_cache     : bf16 [B, max_seq_len, Hkv, D]; rows past s_b are never read
+ *   lse           : fp32 [Hq, total_q] (natural log) or NULL
+ *   cu_seqlens_q  : device int32 [B+1], 4-byte aligned, non-decreasing from 0 to total_q
+ *   seq_lens      : device int32 [B], 4-byte aligned, n_b <= s_b <= max_seq_len
+ *   max_q         : host int, >= every n_b (sizes the grid), <= max_seq_len
+ *   workspace     : >= jl_bifocal_prefill_workspace_size(B, max_seq_len, Hkv, D) bytes
+ *                   (the corrected keys of every sequence; contents ignored on entry)
+ * The device arrays are not read on the host: values outside the contract give an
+ * unspecified result but no access outside q, out, lse or the caches.  A sequence
+ * with n_b = 0 writes nothing.  Each sequence gets what jl_bifocal_prefill_sched
+ * (two-launch form) returns for it alone, with n_q = n_b and n_kv = s_b.  With
+ * every n_b and s_b equal it is that call on the padded batch, with the same
+ * corrected keys and the same sweep; the compiler may fuse the fp32 products of
+ * the query rotation differently in the two kernels, so a rare output differs by
+ * bf16 rounding (jl_plain_prefill_varlen is bitwise jl_plain_prefill).  The
+ * bifocal kernel runs for every sequence, so one with g = 1 is the base model up
+ * to rounding order.  Errors as jl_bifocal_prefill_sched, plus JL_ERR_INVALID_ARG
+ * for NULL or misaligned length arrays, total_q < 1 or max_q > max_seq_len. */
+jl_status jl_bifocal_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                    void* out, float* lse, const int32_t* cu_seqlens_q,
+                                    const int32_t* seq_lens, int32_t batch, int32_t total_q,
+                                    int32_t max_q, int32_t max_seq_len, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                    int64_t local_window, double rope_base, int32_t schedule,
+                                    float softmax_scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Plain causal prefill of a variable-length batch (same layouts, no correction,
+ * no workspace). */
+jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                  void* out, float* lse, const int32_t* cu_seqlens_q,
+                                  const int32_t* seq_lens, int32_t batch, int32_t total_q,
+                                  int32_t max_q, int32_t max_seq_len, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+                                  void* stream);
+
 /* ---- A Qwen3-shaped attention layer ---------------------------------------
  * The method runs inside Qwen3 models of 1.7B, 4B and 8B parameters at up to 128K
  * tokens (seventnews.com, "Empirical results that challenge the status quo").

@@ -318,3 +318,39 @@ def test_layer_workspace_and_validation(lib):
         assert call(attn=0, w=17) == DEVICE      # windows are not checked for the plain layer
         assert lib.jl_qwen3_layer_workspace_size(1, 1, 64, 4, 2, 128) <= need
         assert call(n_new=1) == DEVICE           # one new token: the decode path
+
+
+def test_prefill_varlen_validation(lib):
+    need = lib.jl_bifocal_prefill_workspace_size(2, 100, 2, 128)
+
+    def bif(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, cu=FAKE, sl=FAKE, batch=2, total=150, max_q=100,
+                 n_max=100, hq=4, hkv=2, d=128, L=64, w=16, base=1e4, sched=0, scale=0.0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_bifocal_prefill_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cu"], a["sl"], a["batch"],
+                                             a["total"], a["max_q"], a["n_max"], a["hq"], a["hkv"], a["d"], a["L"],
+                                             a["w"], a["base"], a["sched"], a["scale"], a["ws"], a["wsb"], None)
+
+    def plain(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, cu=FAKE, sl=FAKE, batch=2, total=150, max_q=100,
+                 n_max=100, hq=4, hkv=2, d=128, scale=0.0)
+        a.update(kw)
+        return lib.jl_plain_prefill_varlen(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cu"], a["sl"], a["batch"],
+                                           a["total"], a["max_q"], a["n_max"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                           None)
+
+    for call in (bif, plain):
+        assert call(cu=None) == INVALID
+        assert call(cu=FAKE + 2) == INVALID          # misaligned cu_seqlens_q
+        assert call(sl=None) == INVALID
+        assert call(total=0) == INVALID
+        assert call(max_q=101) == INVALID            # longer than the cache
+        assert call(hq=3) == INVALID
+        assert call(d=64) == UNSUPPORTED
+        assert call(out=FAKE + 8) == INVALID
+        if not _has_gpu():
+            assert call() == DEVICE
+    assert bif(wsb=need - 1) == WORKSPACE
+    assert bif(ws=None) == INVALID
+    assert bif(sched=1, w=64) == INVALID             # seam needs W < L
+    assert bif(w=65) == INVALID

@@ -35,6 +35,8 @@ __all__ = [
     "jl_schedule_factor",
     "jl_bifocal_prefill_sched",
     "jl_bifocal_decode_sched",
+    "jl_bifocal_prefill_varlen",
+    "jl_plain_prefill_varlen",
     "jl_qwen3_layer_workspace_size",
     "jl_qwen3_attention_layer",
 ]
@@ -71,6 +73,10 @@ _SIGNATURES = {
                                         _f64, _i32, _f32, _vp, _sz, _vp]),
     "jl_bifocal_decode_sched": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
                                        _f64, _i32, _f32, _vp, _sz, _vp]),
+    "jl_bifocal_prefill_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _i64, _i64, _f64, _i32, _f32, _vp, _sz, _vp]),
+    "jl_plain_prefill_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _f32, _vp]),
     "jl_qwen3_layer_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "jl_qwen3_attention_layer": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _f32, _i32, _i64, _i64, _f64, _i32, _vp, _sz, _vp]),
@@ -309,3 +315,34 @@ def jl_qwen3_attention_layer(x, w_qkv, q_norm_weight, k_norm_weight, w_o, out, k
         _ptr(v_cache), b, n_new, n_kv, hidden, hq, hkv, d, float(rms_eps), 1 if bifocal else 0,
         int(pretrained_window), int(local_window), float(rope_base), _schedule_id(schedule), _ptr(workspace), nbytes,
         _stream(stream)))
+
+
+def _cu_ptr(cu):
+    import torch
+    if cu.dtype != torch.int32:
+        raise TypeError("cu_seqlens_q must be an int32 device tensor")
+    return _ptr(cu)
+
+
+def jl_bifocal_prefill_varlen(q, k_cache, v_cache, out, lse, cu_seqlens_q, seq_lens, max_q, pretrained_window,
+                              local_window, rope_base, workspace, schedule="grouped", softmax_scale=0.0, stream=None):
+    """q, out [total_q, Hq, D] packed rows; caches [B, max_seq_len, Hkv, D]; lse
+    [Hq, total_q] or None; cu_seqlens_q int32 [B+1] and seq_lens int32 [B] on the
+    device; max_q >= every sequence's new rows; workspace as for
+    jl_bifocal_prefill_ws with n_kv = max_seq_len."""
+    total_q, hq, d = q.shape
+    b, n_max, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_prefill_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _cu_ptr(cu_seqlens_q), _seq_lens_ptr(seq_lens), b,
+        total_q, int(max_q), n_max, hq, hkv, d, int(pretrained_window), int(local_window), float(rope_base),
+        _schedule_id(schedule), float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_plain_prefill_varlen(q, k_cache, v_cache, out, lse, cu_seqlens_q, seq_lens, max_q, softmax_scale=0.0,
+                            stream=None):
+    total_q, hq, d = q.shape
+    b, n_max, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    _check(load_library().jl_plain_prefill_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _cu_ptr(cu_seqlens_q), _seq_lens_ptr(seq_lens), b,
+        total_q, int(max_q), n_max, hq, hkv, d, float(softmax_scale), _stream(stream)))

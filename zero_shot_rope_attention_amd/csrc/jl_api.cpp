@@ -422,6 +422,70 @@ jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void
   return launched(jl::launch_decode(bif, p, static_cast<hipStream_t>(stream)));
 }
 
+static jl_status prefill_varlen_common(const void* q, const void* k, const void* v, void* out,
+                                       const int32_t* cu_seqlens_q, const int32_t* seq_lens, int32_t batch,
+                                       int32_t total_q, int32_t max_q, int32_t max_seq_len, int32_t hq, int32_t hkv,
+                                       int32_t head_dim, float scale_in, float* scale) {
+  JL_TRY(check_pointer(q, "q"));
+  JL_TRY(check_pointer(k, "k_cache"));
+  JL_TRY(check_pointer(v, "v_cache"));
+  JL_TRY(check_pointer(out, "out"));
+  if (!cu_seqlens_q || reinterpret_cast<uintptr_t>(cu_seqlens_q) % 4 != 0)
+    return fail(JL_ERR_INVALID_ARG, "cu_seqlens_q is NULL or not 4-byte aligned");
+  JL_TRY(check_seq_lens(seq_lens));
+  if (total_q < 1) return fail(JL_ERR_INVALID_ARG, "total_q must be >= 1 (got %d)", total_q);
+  const Shape s{batch, max_q, max_seq_len, hq, hkv, head_dim};
+  JL_TRY(check_shape(s));
+  if (elements(total_q, 1, hq) < 0) return fail(JL_ERR_UNSUPPORTED, "tensor sizes overflow 64-bit element offsets");
+  JL_TRY(check_scale(scale_in, scale));
+  return JL_OK;
+}
+
+jl_status jl_bifocal_prefill_varlen(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* seq_lens, int32_t batch,
+                                    int32_t total_q, int32_t max_q, int32_t max_seq_len, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                    int64_t local_window, double rope_base, int32_t schedule, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  float scale;
+  JL_TRY(prefill_varlen_common(q, k_cache, v_cache, out, cu_seqlens_q, seq_lens, batch, total_q, max_q, max_seq_len,
+                               n_q_heads, n_kv_heads, head_dim, softmax_scale, &scale));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(check_schedule(schedule, pretrained_window, local_window, max_seq_len));
+  JL_TRY(check_pointer(workspace, "workspace"));
+  const size_t need = jl_bifocal_prefill_workspace_size(batch, max_seq_len, n_kv_heads, head_dim);
+  if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  JL_TRY(device_check());
+  // the factor, the shift and the rate are taken per sequence in the kernels
+  const int32_t w = (int32_t)(local_window < max_seq_len ? local_window : max_seq_len);
+  jl::PrefillProblem p{q, k_cache, v_cache, out, lse, nullptr, nullptr, workspace, batch, max_q, max_seq_len,
+                       n_q_heads, n_kv_heads, 1, w, rope_base, scale};
+  p.cu_q = cu_seqlens_q;
+  p.kv_lens = seq_lens;
+  p.total_q = total_q;
+  p.schedule = schedule;
+  p.pretrained_window = pretrained_window;
+  return launched(jl::launch_prefill(jl::kModeBifocalPre, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                  const int32_t* cu_seqlens_q, const int32_t* seq_lens, int32_t batch,
+                                  int32_t total_q, int32_t max_q, int32_t max_seq_len, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, float softmax_scale, void* stream) {
+  float scale;
+  JL_TRY(prefill_varlen_common(q, k_cache, v_cache, out, cu_seqlens_q, seq_lens, batch, total_q, max_q, max_seq_len,
+                               n_q_heads, n_kv_heads, head_dim, softmax_scale, &scale));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(device_check());
+  jl::PrefillProblem p{q, k_cache, v_cache, out, lse, nullptr, nullptr, nullptr, batch, max_q, max_seq_len,
+                       n_q_heads, n_kv_heads, 1, 1, 2.0, scale};
+  p.cu_q = cu_seqlens_q;
+  p.kv_lens = seq_lens;
+  p.total_q = total_q;
+  return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
+}
+
 // Workspace of the attention layer: projected q/k/v, rotated queries, the
 // attention output, and the attention's own workspace (corrected keys for the
 // prefill, chunk partials for the decode), each 256-byte aligned.

@@ -48,10 +48,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // The product is reduced to [-1/2, 1/2] revolutions in fp64 (|c| theta_d can
 // reach ~1e5 rad, where an fp32 angle would already be off by ~1e-2 rad); the
 // reduced angle is then evaluated by the hardware sine/cosine, which take
-// revolutions.
+// revolutions.  The reduction is one fused multiply-add, c theta - rint(c theta)
+// with the product unrounded, written out so that every kernel computes the
+// same bits whatever the compiler would contract on its own.
 __device__ __forceinline__ f32x2 rot_cs(long long c, double theta_rev) {
-  const double r = (double)c * theta_rev;
-  const float f = (float)(r - __builtin_rint(r));
+  const double cd = (double)c;
+  const double r = cd * theta_rev;
+  const float f = (float)__builtin_fma(cd, theta_rev, -__builtin_rint(r));
   return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
 }
 

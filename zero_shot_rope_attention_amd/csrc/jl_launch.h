@@ -73,6 +73,17 @@ struct PrefillProblem {
   float softmax_scale;   // > 0
   int32_t q_shift = 0;   // added to c(p) of the queries (seam schedule)
   double rate = 1.0;     // factor on theta for the corrections (fractional schedule)
+  // Variable-length batches (plain and precorrected bifocal modes only): q, out
+  // packed [total_q, Hq, D] with sequence b's rows cu_q[b] .. cu_q[b+1]-1 (device
+  // [B+1]); kv_lens (device [B]) keys per sequence in caches of n_kv rows; lse
+  // [Hq, total_q]; n_q the longest query count.  g, the shift and the rate are then
+  // taken per sequence in the kernels from the fields below (group, q_shift and
+  // rate are not used).
+  const int32_t* cu_q = nullptr;
+  const int32_t* kv_lens = nullptr;
+  int32_t total_q = 0;
+  int32_t schedule = kSchedGrouped;
+  int64_t pretrained_window = 1;
 };
 
 hipError_t launch_prefill(PrefillMode mode, const PrefillProblem& p, hipStream_t stream);

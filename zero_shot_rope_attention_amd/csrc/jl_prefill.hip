@@ -58,6 +58,15 @@ struct PrefillArgs {
   float inv_g;
   float scale_log2;   // softmax scale * log2(e)
   double theta_rev[kHalfD];  // theta_d / (2 pi)
+  // variable-length batches (the VARLEN kernels only): sequence b has the packed
+  // query rows cu_q[b] .. cu_q[b+1]-1 and kv_lens[b] cached keys; n_q is then the
+  // longest query count, n_kv the cache's rows per sequence, and the group factor,
+  // query shift and rate are taken per sequence from big_l, w and sched
+  const int32_t* cu_q;
+  const int32_t* kv_lens;
+  int32_t total_q;
+  int32_t sched;
+  int64_t big_l;
 };
 
 // Swizzled 16-byte chunk of a 256-byte K row: spreads the 32 rows one MFMA
@@ -796,10 +805,19 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
   sc[1] = s1;
 }
 
-template <int MODE>
+// One sequence of a variable-length batch, as the prefill kernel sees it.
+struct SeqView {
+  int n_q, n_kv, n_qblocks, g, q_shift;
+  int64_t q0;   // first packed query row
+  double rate;  // factor on theta (fractional schedule)
+};
+
+template <int MODE, bool VARLEN = false>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
   static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre || MODE == kModeSliding,
                 "ping-pong kernel: plain, bifocal or sliding window");
+  static_assert(!VARLEN || MODE == kModePlain || MODE == kModeBifocalPre,
+                "variable-length batches: plain, or bifocal with corrected keys staged");
   constexpr bool kSliding = MODE == kModeSliding;   // base scores on the window's keys only
   constexpr bool kGrouped = MODE != kModePlain && !kSliding;  // grouped scores on remote keys
   constexpr bool kRotate = MODE == kModeBifocal;    // keys corrected here, tile by tile
@@ -831,25 +849,51 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       rank = id % a.n_qblocks;
     }
   }
-  const int qb = a.n_qblocks - 1 - rank;
+  // The sequence's sizes.  Uniform batches read them from the arguments where they
+  // are used (the accessors below), variable-length batches from the sequence's
+  // entries, clamped: lengths outside the contract give an unspecified result,
+  // never an access out of range.
+  SeqView sv{};
+  if constexpr (VARLEN) {
+    const int bv = unit / (a.grp / a.hpw) / a.hkv;
+    sv.n_kv = min(max(a.kv_lens[bv], 1), a.n_kv);
+    sv.q0 = min(max(a.cu_q[bv], 0), a.total_q);
+    sv.n_q = min(min(max(a.cu_q[bv + 1] - sv.q0, 0), a.total_q - sv.q0), min(a.n_q, sv.n_kv));
+    sv.n_qblocks = (sv.n_q + a.bm - 1) / a.bm;
+    if (rank >= sv.n_qblocks) return;  // a shorter sequence: no query block here
+    if constexpr (MODE == kModeBifocalPre) {
+      sv.g = sched_group(sv.n_kv, a.big_l, a.w, a.sched);
+      sv.q_shift = sched_q_shift(sv.g, a.w, a.sched);
+      sv.rate = sched_rate(sv.n_kv, a.big_l, a.sched);
+    }
+  }
+  // (macros, not lambdas: a lambda capturing the kernel's argument block by
+  // reference makes the compiler copy it to private memory)
+#define SEQ_N_Q (VARLEN ? sv.n_q : a.n_q)
+#define SEQ_N_KV (VARLEN ? sv.n_kv : a.n_kv)
+#define SEQ_G (VARLEN ? sv.g : a.g)
+#define SEQ_Q_SHIFT (VARLEN ? sv.q_shift : a.q_shift)
+#define SEQ_THETA(d) (VARLEN ? a.theta_rev[d] * sv.rate : a.theta_rev[d])
+  const int qb = (VARLEN ? sv.n_qblocks : a.n_qblocks) - 1 - rank;
   const int n_hg = a.grp / a.hpw;
   const int hg = unit % n_hg;
   const int bk = unit / n_hg;
   const int kvh = bk % a.hkv;
   const int b = bk / a.hkv;
+#define SEQ_Q0 (VARLEN ? sv.q0 : (int64_t)b * a.n_q)
   const int hq = kvh * a.grp + hg * a.hpw + (wave % a.hpw);
   const int row0_wg = qb * a.bm;
   const int row0 = row0_wg + (wave / a.hpw) * 32;
-  const int pos_off = a.n_kv - a.n_q;
-  const int last_row_wg = min(a.n_q, row0_wg + a.bm) - 1;
+  const int pos_off = SEQ_N_KV - SEQ_N_Q;
+  const int last_row_wg = min(SEQ_N_Q, row0_wg + a.bm) - 1;
   const int kend = pos_off + last_row_wg + 1;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  const bool wave_rows = row0 < a.n_q;
+  const bool wave_rows = row0 < SEQ_N_Q;
   const int wp_lo = pos_off + row0;
-  const int wp_hi = pos_off + min(a.n_q, row0 + 32) - 1;
+  const int wp_hi = pos_off + min(SEQ_N_Q, row0 + 32) - 1;
   const int my_row = row0 + (lane & 31);
-  const bool row_ok = my_row < a.n_q;
+  const bool row_ok = my_row < SEQ_N_Q;
   const int my_p = row_ok ? pos_off + my_row : -1;
 
   const int64_t q_rs = (int64_t)a.hq * kD;
@@ -887,12 +931,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   }
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
-  load_half(regs, k_src(t0), vbase, kv_rs, a.n_kv, t0 * kBN, soff);
+  load_half(regs, k_src(t0), vbase, kv_rs, SEQ_N_KV, t0 * kBN, soff);
 
   bf16x8 qf[8];
   bf16x8 qg[8];
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
     u32x4 raw[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -900,7 +944,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       qf[kk] = as_bf16x8(raw[kk]);
     }
     if constexpr (kGrouped) {
-      const long long cq = row_ok ? (long long)(my_p / a.g) - my_p + a.q_shift : 0;
+      const long long cq = row_ok ? (long long)(my_p / SEQ_G) - my_p + SEQ_Q_SHIFT : 0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         u32x4 lo, hi;
@@ -910,7 +954,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int e = 2 * e2 + t;
-            const f32x2 cs = rot_cs(cq, a.theta_rev[16 * kk + 8 * h + e]);
+            const f32x2 cs = rot_cs(cq, SEQ_THETA(16 * kk + 8 * h + e));
             const float x1 = elem(raw[kk], e), x2 = elem(raw[kk + 4], e);
             y1[t] = x1 * cs.x - x2 * cs.y;
             y2[t] = x2 * cs.x + x1 * cs.y;
@@ -934,7 +978,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
                         gtid);
       if (tt >= n_interior && tt < t_local) {  // edge tile: the corrected keys too
         HalfTile kgr;
-        load_k_only(kgr, kgbase, kv_rs, a.n_kv, tt * kBN, soff);
+        load_k_only(kgr, kgbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
         store_k_only(kgr, s_kg + (tt & 1) * kTileBytes, grp, gtid);
       }
     } else {
@@ -960,7 +1004,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       if (gtid < 64) base_angles(1, 2 * grp);
       __syncthreads();
     }
-    load_half(regs, k_src(t0 + 1), vbase, kv_rs, a.n_kv, (t0 + 1) * kBN, soff);
+    load_half(regs, k_src(t0 + 1), vbase, kv_rs, SEQ_N_KV, (t0 + 1) * kBN, soff);
     store(t0 + 1, 2 * grp);
   }
   if constexpr (kRotate) {
@@ -1011,7 +1055,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // bifocal: they are issued at the start of the VALU phase, so that the 16
     // registers they fill are not live across the MFMA phase, where that kernel
     // has none left
-    if (!kRotate && do_stage) load_half(regs, k_src(tt), vbase, kv_rs, a.n_kv, tt * kBN, soff);
+    if (!kRotate && do_stage) load_half(regs, k_src(tt), vbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
     // V of tile k-1 (at the first tile the probabilities are zero and that
@@ -1051,7 +1095,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xs[0][kb][i]));
     }
-    if (kRotate && do_stage) load_half(regs, kbase, vbase, kv_rs, a.n_kv, tt * kBN, soff);
+    if (kRotate && do_stage) load_half(regs, kbase, vbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
@@ -1078,7 +1122,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     for (; k < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{});
   if constexpr (kGrouped) {
     // the base-RoPE query fragment is only needed from the band on
-    const uint16_t* qrow = a.q + ((int64_t)b * a.n_q + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
@@ -1094,7 +1138,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   const float lt = half_sum(l_run[0]);
   const float inv = 1.0f / lt;
   const float lse_v = (m_run[0] * a.scale_log2 + __builtin_log2f(lt)) * kLn2;
-  uint16_t* o = a.out + (((int64_t)b * a.n_q + my_row) * a.hq + hq) * kD;
+  uint16_t* o = a.out + ((SEQ_Q0 + my_row) * a.hq + hq) * kD;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -1103,8 +1147,19 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
                    pack_bf16(acc[0][nb][4 * i4 + 2] * inv, acc[0][nb][4 * i4 + 3] * inv)};
       *reinterpret_cast<u32x2*>(o + 32 * nb + 8 * i4 + 4 * h) = val;
     }
-  if (a.lse && h == 0) a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = lse_v;
+  if (a.lse && h == 0) {
+    // lse: [B, Hq, n_q] for uniform batches, [Hq, total_q] over the packed rows otherwise
+    if constexpr (VARLEN) a.lse[(int64_t)hq * a.total_q + sv.q0 + my_row] = lse_v;
+    else a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = lse_v;
+  }
 }
+
+#undef SEQ_N_Q
+#undef SEQ_N_KV
+#undef SEQ_G
+#undef SEQ_Q_SHIFT
+#undef SEQ_THETA
+#undef SEQ_Q0
 
 // ---------------------------------------------------------------------------
 // Corrected keys of the whole cache, for the precorrected mode:
@@ -1118,17 +1173,33 @@ struct CorrectArgs {
   int64_t rows;  // batch * n_kv
   int32_t n_kv, hkv, g;
   double theta_rev[kHalfD];
+  // variable-length batches: keys per sequence (rows past them are skipped), with
+  // g and the rate taken per sequence; null for uniform batches
+  const int32_t* kv_lens;
+  int64_t big_l;
+  int32_t w, sched;
 };
 
+template <bool VARLEN>
 __global__ __launch_bounds__(256) void correct_keys_kernel(const CorrectArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int c = threadIdx.x & 7;
   if (row >= a.rows) return;
   const int j = (int)(row % a.n_kv);
-  const long long cj = (long long)(j / a.g) - j;
   f32x2 cs[8];
+  if constexpr (VARLEN) {
+    const int s_b = min(max(a.kv_lens[row / a.n_kv], 1), a.n_kv);
+    if (j >= s_b) return;  // past the sequence's keys: never read
+    const int g = sched_group(s_b, a.big_l, a.w, a.sched);
+    const double rate = sched_rate(s_b, a.big_l, a.sched);
+    const long long cj = (long long)(j / g) - j;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) cs[e] = rot_cs(cj, a.theta_rev[8 * c + e]);
+    for (int e = 0; e < 8; ++e) cs[e] = rot_cs(cj, a.theta_rev[8 * c + e] * rate);
+  } else {
+    const long long cj = (long long)(j / a.g) - j;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs[e] = rot_cs(cj, a.theta_rev[8 * c + e]);
+  }
   for (int hh = 0; hh < a.hkv; ++hh) {
     const int64_t base = (row * a.hkv + hh) * kD + 8 * c;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(a.k + base);
@@ -1183,6 +1254,12 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   a.w = p.local_window;
   a.q_shift = p.q_shift;
   a.inv_g = 1.0f / (float)p.group;
+  a.cu_q = p.cu_q;
+  a.kv_lens = p.kv_lens;
+  a.total_q = p.total_q;
+  a.sched = p.schedule;
+  a.big_l = p.pretrained_window;
+  if (p.cu_q && !(MODE == kModePlain || MODE == kModeBifocalPre)) return hipErrorInvalidValue;
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   // theta_d / (2 pi), times the schedule's rate (1 but for the fractional one)
   const double two_pi = 6.283185307179586476925286766559;
@@ -1199,13 +1276,25 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
     c.hkv = p.n_kv_heads;
     c.g = p.group;
     for (int d = 0; d < kHalfD; ++d) c.theta_rev[d] = a.theta_rev[d];
+    c.kv_lens = p.kv_lens;
+    c.big_l = p.pretrained_window;
+    c.w = p.local_window;
+    c.sched = p.schedule;
     const long long cblocks = (c.rows + 31) / 32;
     if (cblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(correct_keys_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream, c);
+    if (p.kv_lens)
+      hipLaunchKernelGGL(correct_keys_kernel<true>, dim3((unsigned)cblocks), dim3(256), 0, stream, c);
+    else
+      hipLaunchKernelGGL(correct_keys_kernel<false>, dim3((unsigned)cblocks), dim3(256), 0, stream, c);
   }
   if constexpr (MODE == kModePasses)
     hipLaunchKernelGGL((prefill_kernel<MODE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
-  else
+  else if constexpr (MODE == kModePlain || MODE == kModeBifocalPre) {
+    if (p.cu_q)
+      hipLaunchKernelGGL((prefill_pp_kernel<MODE, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_pp_kernel<MODE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+  } else
     hipLaunchKernelGGL((prefill_pp_kernel<MODE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
