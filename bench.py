@@ -117,6 +117,49 @@ def cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, n_rows, seed=0):
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
+def bench_prefill_varlen(jl, torch, s, hq, hkv, big_l, w, base, args):
+    """A variable-length prefill batch: 4 whole prompts of s/8, s/4, 3s/8 and s/2 tokens
+    (16K..64K at 128K), packed, each with its own factor (g = 1, 1, 2, 2 at L = 32K);
+    TFLOP/s on the algorithmic count of every sequence's causal pairs."""
+    dev = torch.device("cuda:0")
+    lens = [s // 8, s // 4, 3 * s // 8, s // 2]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321)
+    total = sum(lens)
+    n_max = max(lens)
+    q = torch.randn(total, hq, 128, generator=gen, device=dev).to(torch.bfloat16)
+    kc = torch.randn(len(lens), n_max, hkv, 128, generator=gen, device=dev).to(torch.bfloat16)
+    vc = torch.randn(len(lens), n_max, hkv, 128, generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ws = torch.empty(jl.jl_bifocal_prefill_workspace_size(len(lens), n_max, hkv), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    flops = sum(prefill_flops(1, x, hq) for x in lens)
+    res = {"seq_lens": lens, "g": [jl.jl_group_factor(x, big_l) for x in lens], "flops": flops,
+           "data": "seeded device normals"}
+    for name in ("bifocal", "plain"):
+        def call():
+            if name == "bifocal":
+                jl.jl_bifocal_prefill_varlen(q, kc, vc, out, None, cu, sl, n_max, big_l, w, base, ws)
+            else:
+                jl.jl_plain_prefill_varlen(q, kc, vc, out, None, cu, sl, n_max)
+        call()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            call()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        res[name] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    res["overhead_vs_plain"] = round(res["bifocal"]["ms"] / res["plain"]["ms"] - 1.0, 4)
+    log(f"prefill varlen {lens}: bifocal {res['bifocal']['ms']:.2f} ms ({res['bifocal']['tflops']} TFLOP/s), "
+        f"plain {res['plain']['ms']:.2f} ms")
+    del q, kc, vc, out, ws
+    return res
+
+
 def bench_layer(jl, torch, s, hq, hkv, big_l, w, base, args, result):
     """One Qwen3-8B-shaped attention layer (hidden 4096) at this length: prefill of the
     whole prompt and one decode step, with the bifocal attention and with plain attention.
@@ -504,6 +547,7 @@ def main():
             del kv_b, vv_b
 
     if not args.no_extras and b == 1:
+        result["prefill_varlen"] = bench_prefill_varlen(jl, torch, s, hq, hkv, big_l, w, base, args)
         result["layer"] = bench_layer(jl, torch, s, hq, hkv, big_l, w, base, args, result)
 
     if not args.no_cpu_baseline:
