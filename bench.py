@@ -339,10 +339,10 @@ def main():
                    "group_factor": g},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "prefill_pp_kernel<3> (bifocal, corrected keys staged) + correct_keys_kernel",
+                     "kernel": "prefill_pp_kernel<3, false> (bifocal, corrected keys staged) + correct_keys_kernel<false>",
                      "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
                      "timing": "HIP events around the whole prefill call (both launches) on its stream",
-                     "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3>: rocprofv3 FETCH_SIZE x 2.0 + "
+                     "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3, false>: rocprofv3 FETCH_SIZE x 2.0 + "
                                      "WRITE_SIZE x 1.0 (scales from a 1 GiB copy), null if the kernel changed since"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
         "decode_in_step_us": round(float(np.mean(dec_ms)) * 1e3, 2),
