@@ -27,6 +27,10 @@ Parity pins (see ``tests/test_oracle_*.py``):
 * ``bifocal_bruteforce``: same pins as above (they check each other) plus the
   D=2 closed form, which uses neither.
 * ``plain_causal_attention``: torch fp64 ``scaled_dot_product_attention``.
+* ``positions`` (explicit query positions, any of the functions above): rows at
+  given positions equal the rows of the whole prefill at those positions; the
+  three-pass form equals the brute force; plain equals torch's fp64 attention
+  with the matching causal mask.
 * ``bifocal_decode``: it is ``bifocal_three_pass`` at one query row, pinned by the
   same tests plus the decode-equals-last-prefill-row check.
 * ``long_range_schedule`` (seam-shifted and fractional variants): the three-pass
@@ -182,11 +186,18 @@ def long_range_schedule(seq_len: int, pretrained_window: int, local_window: int,
     raise ValueError(f"unknown schedule {schedule!r}")
 
 
-def query_positions(n_q: int, n_kv: int) -> np.ndarray:
-    """Positions of the queries: the newest n_q tokens of an n_kv-key context."""
+def query_positions(n_q: int, n_kv: int, positions=None) -> np.ndarray:
+    """Positions of the queries: the newest n_q tokens of an n_kv-key context, or
+    the given ``positions`` (one per query row, each in [0, n_kv)): the queries of
+    a chunk need not be contiguous nor the newest tokens."""
     if n_q > n_kv:
         raise ValueError("n_q must be <= n_kv")
-    return np.arange(n_kv - n_q, n_kv, dtype=np.int64)
+    if positions is None:
+        return np.arange(n_kv - n_q, n_kv, dtype=np.int64)
+    pos = np.asarray(positions, dtype=np.int64)
+    if pos.shape != (n_q,) or (n_q and (pos.min() < 0 or pos.max() >= n_kv)):
+        raise ValueError("positions must hold one position in [0, n_kv) per query row")
+    return pos
 
 
 # ---------------------------------------------------------------------------
@@ -308,17 +319,18 @@ def _check_shapes(q, k, v):
 # Plain causal attention (the base model; exact-recovery target)
 # ---------------------------------------------------------------------------
 
-def plain_causal_attention(q, k, v, softmax_scale=None, rows=None, row_block=256):
+def plain_causal_attention(q, k, v, softmax_scale=None, rows=None, row_block=256, positions=None):
     """Causal softmax attention on the cached (original-position) vectors.
 
     Returns ``(out [B, R, Hq, D], lse [B, Hq, R])`` for the selected query rows
     (all rows by default).  GQA: query head h reads KV head h // (Hq / Hkv).
+    ``positions``: the query rows' positions (``query_positions``).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     b, n_q, n_kv, hq, hkv, d = _check_shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if not softmax_scale or softmax_scale <= 0 else float(softmax_scale)
     rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
-    pos = query_positions(n_q, n_kv)
+    pos = query_positions(n_q, n_kv, positions)
     grp = hq // hkv
     out = np.zeros((b, len(rows), hq, d))
     lse = np.zeros((b, hq, len(rows)))
@@ -343,7 +355,7 @@ def plain_causal_attention(q, k, v, softmax_scale=None, rows=None, row_block=256
 # ---------------------------------------------------------------------------
 
 def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
-                       softmax_scale=None, rows=None, row_block=128, schedule="grouped"):
+                       softmax_scale=None, rows=None, row_block=128, schedule="grouped", positions=None):
     """Bifocal attention as three FlashAttention-style passes and their merge.
 
     ResearchPod summary, 2nd paragraph (three passes, smallest integer grouping);
@@ -366,7 +378,9 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
     shift; g from s = n_kv; local iff p_i - j <= W - 1; tau = 1/sqrt(D) unless
     given; GQA head h -> KV head h // (Hq/Hkv).  ``schedule`` selects another
     long-range schedule (``long_range_schedule``): the corrections become
-    rot(q, (a_q(p) - p) theta) and rot(k, (a_k(j) - j) theta).
+    rot(q, (a_q(p) - p) theta) and rot(k, (a_k(j) - j) theta).  ``positions``
+    gives the query rows' positions (``query_positions``); g still comes from
+    s = n_kv.
 
     Returns a dict with ``out [B, R, Hq, D]``, ``lse [B, Hq, R]`` (natural log),
     ``passes`` = {"A": (O, lse), "B": ..., "C": ...} with the same shapes, and
@@ -381,7 +395,7 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
     scale = 1.0 / math.sqrt(d) if not softmax_scale or softmax_scale <= 0 else float(softmax_scale)
     g, a_q, a_k = long_range_schedule(n_kv, big_l, w_loc, schedule)
     theta = rope_frequencies(d, rope_base)
-    pos = query_positions(n_q, n_kv)
+    pos = query_positions(n_q, n_kv, positions)
     rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
     grp = hq // hkv
 
@@ -471,7 +485,7 @@ def _default_selection(g: int, local_window: int):
 
 
 def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_base,
-                       softmax_scale=None, select=None, schedule="grouped"):
+                       softmax_scale=None, select=None, schedule="grouped", positions=None):
     """Bifocal attention written as one masked softmax with a per-pair choice of
     positions, on *raw* (un-rotated) q and k.  Pure Python loops over pairs and
     explicit D x D rotation matrices; for tiny inputs only.
@@ -503,7 +517,7 @@ def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_ba
                 return p, j
             return float(a_q(p)), float(a_k(j))
     theta = rope_frequencies(d, rope_base)
-    pos = query_positions(n_q, n_kv)
+    pos = query_positions(n_q, n_kv, positions)
     grp = hq // hkv
     mats = {}
 

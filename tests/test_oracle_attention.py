@@ -453,3 +453,30 @@ def test_prefill_varlen_equals_bruteforce_per_sequence():
         mask = torch.from_numpy(np.arange(s)[None, :] <= (s - n + np.arange(n))[:, None])
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask).permute(0, 2, 1, 3)
         assert np.abs(out_p[cu[bi]:cu[bi + 1]] - ref.numpy()[0]).max() <= 1e-12
+
+
+@pytest.mark.parametrize("schedule", list(oracle.SCHEDULES))
+def test_explicit_positions_are_rows_of_the_whole_prefill(schedule):
+    # queries at a sorted subset of positions (gaps, repeats) of a 90-key context
+    s, big_l, w, d, hq, hkv, base = 90, 16, 5, 16, 4, 2, 1e4
+    rng = np.random.default_rng(90)
+    pos = np.sort(rng.choice(s, 23, replace=True))
+    q_raw, k_raw, v = _raw_inputs(91, 1, s, s, hq, hkv, d)
+    q_all, k = _prerotate(q_raw, k_raw, base)
+    full = oracle.bifocal_three_pass(q_all, k, v, big_l, w, base, schedule=schedule)
+    r = oracle.bifocal_three_pass(q_all[:, pos], k, v, big_l, w, base, schedule=schedule, positions=pos)
+    assert np.abs(r["out"] - full["out"][:, pos]).max() <= 1e-12
+    assert np.abs(r["lse"] - full["lse"][:, :, pos]).max() <= 1e-12
+    o2, l2 = oracle.bifocal_bruteforce(q_raw[:, pos], k_raw, v, big_l, w, base, schedule=schedule, positions=pos)
+    assert np.abs(r["out"] - o2).max() <= 1e-12 and np.abs(r["lse"] - l2).max() <= 1e-11
+    if schedule == "grouped":
+        op, lp = oracle.plain_causal_attention(q_all[:, pos], k, v, positions=pos)
+        mask = torch.from_numpy(np.arange(s)[None, :] <= pos[:, None])
+        rep = hq // hkv
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q_all[:, pos]).permute(0, 2, 1, 3),
+            torch.from_numpy(np.repeat(k, rep, axis=2)).permute(0, 2, 1, 3),
+            torch.from_numpy(np.repeat(v, rep, axis=2)).permute(0, 2, 1, 3), attn_mask=mask).permute(0, 2, 1, 3)
+        assert np.abs(op - ref.numpy()).max() <= 1e-12
+    with pytest.raises(ValueError):
+        oracle.query_positions(3, 10, [0, 4, 10])
