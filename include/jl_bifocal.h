@@ -327,6 +327,34 @@ jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void
                                   int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
                                   void* stream);
 
+/* ---- Explicit query positions ----------------------------------------------
+ * The query rows of a call need not be the newest tokens: row i sits at position
+ * q_pos[i] of the n_kv-key context (ResearchPod transcript, cache exchange: the
+ * cache keeps original positions, so any query can be scored against it), with g
+ * from s = n_kv.  This serves, for instance, several candidate continuations or
+ * rows recomputed in place.
+ *   q_pos : device int32 [n_q], 4-byte aligned, nondecreasing, each in [0, n_kv),
+ *           shared by every sequence of the batch; not read on the host: values
+ *           outside the contract give an unspecified result, never an access out
+ *           of range (positions are clamped into [0, n_kv))
+ * Everything else as jl_bifocal_prefill_sched in its two-launch form (the
+ * workspace is needed when g > 1) and jl_plain_prefill.  Row i gets what the
+ * whole prefill of n_kv queries gives at position q_pos[i], up to rounding
+ * order.  Errors as those calls, plus JL_ERR_INVALID_ARG for a NULL or
+ * misaligned q_pos. */
+jl_status jl_bifocal_prefill_positions(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, const int32_t* q_pos, int32_t batch, int32_t n_q,
+                                       int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t head_dim, int64_t pretrained_window,
+                                       int64_t local_window, double rope_base, int32_t schedule,
+                                       float softmax_scale, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v, void* out,
+                                     float* lse, const int32_t* q_pos, int32_t batch, int32_t n_q,
+                                     int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, float softmax_scale, void* stream);
+
 /* ---- A Qwen3-shaped attention layer ---------------------------------------
  * The method runs inside Qwen3 models of 1.7B, 4B and 8B parameters at up to 128K
  * tokens (seventnews.com, "Empirical results that challenge the status quo").

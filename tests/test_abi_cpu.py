@@ -354,3 +354,34 @@ def test_prefill_varlen_validation(lib):
     assert bif(ws=None) == INVALID
     assert bif(sched=1, w=64) == INVALID             # seam needs W < L
     assert bif(w=65) == INVALID
+
+
+def test_prefill_positions_validation(lib):
+    need = lib.jl_bifocal_prefill_workspace_size(1, 100, 2, 128)
+
+    def bif(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, pos=FAKE, batch=1, n_q=10, n_kv=100, hq=4, hkv=2, d=128,
+                 L=32, w=8, base=1e4, sched=0, scale=0.0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_bifocal_prefill_positions(a["q"], a["k"], a["v"], a["out"], a["lse"], a["pos"], a["batch"],
+                                                a["n_q"], a["n_kv"], a["hq"], a["hkv"], a["d"], a["L"], a["w"],
+                                                a["base"], a["sched"], a["scale"], a["ws"], a["wsb"], None)
+
+    def plain(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, pos=FAKE, batch=1, n_q=10, n_kv=100, hq=4, hkv=2, d=128,
+                 scale=0.0)
+        a.update(kw)
+        return lib.jl_plain_prefill_positions(a["q"], a["k"], a["v"], a["out"], a["lse"], a["pos"], a["batch"],
+                                              a["n_q"], a["n_kv"], a["hq"], a["hkv"], a["d"], a["scale"], None)
+
+    for call in (bif, plain):
+        assert call(pos=None) == INVALID
+        assert call(pos=FAKE + 2) == INVALID
+        assert call(n_q=101) == INVALID
+        assert call(d=64) == UNSUPPORTED
+        if not _has_gpu():
+            assert call() == DEVICE
+    assert bif(wsb=need - 1) == WORKSPACE
+    assert bif(sched=1, w=32) == INVALID
+    if not _has_gpu():
+        assert bif(L=128, ws=None, wsb=0) == DEVICE      # g = 1: no workspace needed

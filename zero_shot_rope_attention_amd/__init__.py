@@ -37,6 +37,8 @@ __all__ = [
     "jl_bifocal_decode_sched",
     "jl_bifocal_prefill_varlen",
     "jl_plain_prefill_varlen",
+    "jl_bifocal_prefill_positions",
+    "jl_plain_prefill_positions",
     "jl_qwen3_layer_workspace_size",
     "jl_qwen3_attention_layer",
 ]
@@ -77,6 +79,10 @@ _SIGNATURES = {
                                          _i32, _i64, _i64, _f64, _i32, _f32, _vp, _sz, _vp]),
     "jl_plain_prefill_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                        _f32, _vp]),
+    "jl_bifocal_prefill_positions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                            _i64, _f64, _i32, _f32, _vp, _sz, _vp]),
+    "jl_plain_prefill_positions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                          _vp]),
     "jl_qwen3_layer_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "jl_qwen3_attention_layer": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _f32, _i32, _i64, _i64, _f64, _i32, _vp, _sz, _vp]),
@@ -346,3 +352,31 @@ def jl_plain_prefill_varlen(q, k_cache, v_cache, out, lse, cu_seqlens_q, seq_len
     _check(load_library().jl_plain_prefill_varlen(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _cu_ptr(cu_seqlens_q), _seq_lens_ptr(seq_lens), b,
         total_q, int(max_q), n_max, hq, hkv, d, float(softmax_scale), _stream(stream)))
+
+
+def _pos_ptr(q_pos):
+    import torch
+    if q_pos.dtype != torch.int32:
+        raise TypeError("q_pos must be an int32 device tensor")
+    return _ptr(q_pos)
+
+
+def jl_bifocal_prefill_positions(q, k, v, out, lse, q_pos, pretrained_window, local_window, rope_base,
+                                 workspace=None, schedule="grouped", softmax_scale=0.0, stream=None):
+    """As jl_bifocal_prefill_ws, with query row i at position q_pos[i] (int32 device
+    tensor [n_q], nondecreasing); the workspace may be None when g = 1."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_prefill_positions(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _pos_ptr(q_pos), b, n_q, n_kv, hq, hkv, d,
+        int(pretrained_window), int(local_window), float(rope_base), _schedule_id(schedule), float(softmax_scale),
+        _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_plain_prefill_positions(q, k, v, out, lse, q_pos, softmax_scale=0.0, stream=None):
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    _check(load_library().jl_plain_prefill_positions(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                     _pos_ptr(q_pos), b, n_q, n_kv, hq, hkv, d, float(softmax_scale),
+                                                     _stream(stream)))

@@ -486,6 +486,60 @@ jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void
   return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
 }
 
+static jl_status check_positions(const int32_t* q_pos) {
+  if (!q_pos) return fail(JL_ERR_INVALID_ARG, "q_pos is NULL");
+  if (reinterpret_cast<uintptr_t>(q_pos) % 4 != 0) return fail(JL_ERR_INVALID_ARG, "q_pos is not 4-byte aligned");
+  return JL_OK;
+}
+
+jl_status jl_bifocal_prefill_positions(const void* q, const void* k, const void* v, void* out, float* lse,
+                                       const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       int64_t pretrained_window, int64_t local_window, double rope_base,
+                                       int32_t schedule, float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_positions(q_pos));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(check_schedule(schedule, pretrained_window, local_window, n_kv));
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  const int32_t g = jl::sched_group(n_kv, pretrained_window, w, schedule);
+  if (g > 1) {
+    JL_TRY(check_pointer(workspace, "workspace"));
+    const size_t need = jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim);
+    if (workspace_bytes < need)
+      return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  }
+  JL_TRY(device_check());
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, g > 1 ? workspace : nullptr, batch, n_q, n_kv,
+                       n_q_heads, n_kv_heads, g, w, rope_base, scale};
+  p.q_shift = jl::sched_q_shift(g, w, schedule);
+  p.rate = jl::sched_rate(n_kv, pretrained_window, schedule);
+  p.q_pos = q_pos;
+  return launched(jl::launch_prefill(g > 1 ? jl::kModeBifocalPre : jl::kModePlain, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv,
+                                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
+                                     void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_positions(q_pos));
+  JL_TRY(device_check());
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, 1,
+                       2.0, scale};
+  p.q_pos = q_pos;
+  return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
+}
+
 // Workspace of the attention layer: projected q/k/v, rotated queries, the
 // attention output, and the attention's own workspace (corrected keys for the
 // prefill, chunk partials for the decode), each 256-byte aligned.

@@ -84,6 +84,9 @@ struct PrefillProblem {
   int32_t total_q = 0;
   int32_t schedule = kSchedGrouped;
   int64_t pretrained_window = 1;
+  // Explicit query positions (plain and precorrected bifocal modes, uniform
+  // batches): device int32 [n_q], nondecreasing, in [0, n_kv); null: n_kv - n_q + i.
+  const int32_t* q_pos = nullptr;
 };
 
 hipError_t launch_prefill(PrefillMode mode, const PrefillProblem& p, hipStream_t stream);

@@ -67,6 +67,9 @@ struct PrefillArgs {
   int32_t total_q;
   int32_t sched;
   int64_t big_l;
+  // explicit query positions (the QPOS kernels only): row i sits at q_pos[i],
+  // nondecreasing, shared by the batch; otherwise row i sits at n_kv - n_q + i
+  const int32_t* q_pos;
 };
 
 // Swizzled 16-byte chunk of a 256-byte K row: spreads the 32 rows one MFMA
@@ -812,12 +815,13 @@ struct SeqView {
   double rate;  // factor on theta (fractional schedule)
 };
 
-template <int MODE, bool VARLEN = false>
+template <int MODE, bool VARLEN = false, bool QPOS = false>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
   static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre || MODE == kModeSliding,
                 "ping-pong kernel: plain, bifocal or sliding window");
-  static_assert(!VARLEN || MODE == kModePlain || MODE == kModeBifocalPre,
-                "variable-length batches: plain, or bifocal with corrected keys staged");
+  static_assert(!(VARLEN || QPOS) || MODE == kModePlain || MODE == kModeBifocalPre,
+                "variable-length batches and explicit positions: plain, or bifocal with corrected keys staged");
+  static_assert(!(VARLEN && QPOS), "explicit positions are for uniform batches");
   constexpr bool kSliding = MODE == kModeSliding;   // base scores on the window's keys only
   constexpr bool kGrouped = MODE != kModePlain && !kSliding;  // grouped scores on remote keys
   constexpr bool kRotate = MODE == kModeBifocal;    // keys corrected here, tile by tile
@@ -885,16 +889,20 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   const int row0_wg = qb * a.bm;
   const int row0 = row0_wg + (wave / a.hpw) * 32;
   const int pos_off = SEQ_N_KV - SEQ_N_Q;
+  // position of query row r: explicit positions are clamped into the context
+  // (positions outside the contract give an unspecified result, never an access
+  // out of range); tiles are classified from the first and last rows' positions
+#define SEQ_POS(r) (QPOS ? min(max(a.q_pos[(r)], 0), SEQ_N_KV - 1) : pos_off + (r))
   const int last_row_wg = min(SEQ_N_Q, row0_wg + a.bm) - 1;
-  const int kend = pos_off + last_row_wg + 1;
+  const int kend = QPOS ? SEQ_POS(last_row_wg) + 1 : pos_off + last_row_wg + 1;
   const int ntiles = (kend + kBN - 1) / kBN;
 
   const bool wave_rows = row0 < SEQ_N_Q;
-  const int wp_lo = pos_off + row0;
-  const int wp_hi = pos_off + min(SEQ_N_Q, row0 + 32) - 1;
+  const int wp_lo = QPOS ? SEQ_POS(min(row0, SEQ_N_Q - 1)) : pos_off + row0;
+  const int wp_hi = QPOS ? SEQ_POS(min(SEQ_N_Q, row0 + 32) - 1) : pos_off + min(SEQ_N_Q, row0 + 32) - 1;
   const int my_row = row0 + (lane & 31);
   const bool row_ok = my_row < SEQ_N_Q;
-  const int my_p = row_ok ? pos_off + my_row : -1;
+  const int my_p = row_ok ? (QPOS ? SEQ_POS(my_row) : pos_off + my_row) : -1;
 
   const int64_t q_rs = (int64_t)a.hq * kD;
   const int64_t kv_rs = (int64_t)a.hkv * kD;
@@ -903,7 +911,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   const uint16_t* kgbase = kPre ? a.kg + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD : nullptr;
 
   // tile kinds of this workgroup's rows [p0, p1] (see the tile program below)
-  const int p0_wg = pos_off + row0_wg;
+  const int p0_wg = QPOS ? SEQ_POS(row0_wg) : pos_off + row0_wg;
   int n_interior = 0;
   if constexpr (MODE == kModePlain) n_interior = min(ntiles, max(0, (p0_wg + 1) / kBN));
   if constexpr (kGrouped) n_interior = min(ntiles, max(0, (p0_wg - a.w + 1) / kBN));
@@ -914,7 +922,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   // first tile whose causal keys are local for every row of the workgroup
   int t_local = n_interior;
   if constexpr (kGrouped || kSliding) {
-    const int first_all_local = pos_off + last_row_wg - a.w + 1;
+    const int first_all_local = (QPOS ? SEQ_POS(last_row_wg) : pos_off + last_row_wg) - a.w + 1;
     t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
     t_local = min(ntiles, max(n_interior, t_local));
   }
@@ -1155,6 +1163,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 }
 
 #undef SEQ_N_Q
+#undef SEQ_POS
 #undef SEQ_N_KV
 #undef SEQ_G
 #undef SEQ_Q_SHIFT
@@ -1259,7 +1268,9 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   a.total_q = p.total_q;
   a.sched = p.schedule;
   a.big_l = p.pretrained_window;
-  if (p.cu_q && !(MODE == kModePlain || MODE == kModeBifocalPre)) return hipErrorInvalidValue;
+  a.q_pos = p.q_pos;
+  if ((p.cu_q || p.q_pos) && !(MODE == kModePlain || MODE == kModeBifocalPre)) return hipErrorInvalidValue;
+  if (p.cu_q && p.q_pos) return hipErrorInvalidValue;
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   // theta_d / (2 pi), times the schedule's rate (1 but for the fractional one)
   const double two_pi = 6.283185307179586476925286766559;
@@ -1292,6 +1303,9 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   else if constexpr (MODE == kModePlain || MODE == kModeBifocalPre) {
     if (p.cu_q)
       hipLaunchKernelGGL((prefill_pp_kernel<MODE, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    else if (p.q_pos)
+      hipLaunchKernelGGL((prefill_pp_kernel<MODE, false, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                         a);
     else
       hipLaunchKernelGGL((prefill_pp_kernel<MODE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   } else
