@@ -385,3 +385,41 @@ def test_prefill_positions_validation(lib):
     assert bif(sched=1, w=32) == INVALID
     if not _has_gpu():
         assert bif(L=128, ws=None, wsb=0) == DEVICE      # g = 1: no workspace needed
+
+
+def _header_signatures():
+    """name -> (return type, [parameter types]) from the header's declarations."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"#.*", "", text)
+    sigs = {}
+    for m in re.finditer(r"([A-Za-z_][A-Za-z_0-9 \*]*?)\b(jl_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", text):
+        ret, name, params = m.group(1).strip(), m.group(2), m.group(3).strip()
+        types = []
+        if params and params != "void":
+            for p_ in params.split(","):
+                p_ = " ".join(p_.split())
+                types.append(re.sub(r"\s*\b[a-z_0-9]+$", "", p_) if not p_.endswith("*") else p_)
+        sigs[name] = (ret, types)
+    return sigs
+
+
+def test_binding_signatures_match_the_header():
+    # every ctypes declaration must have the header's parameter count and kinds:
+    # pointers as c_void_p (or char* for the message), int32/int64/size_t/float/double alike
+    import ctypes
+    kinds = {"int32_t": ctypes.c_int32, "jl_status": ctypes.c_int32, "int64_t": ctypes.c_int64,
+             "size_t": ctypes.c_size_t, "float": ctypes.c_float, "double": ctypes.c_double}
+    sigs = _header_signatures()
+    assert set(sigs) == set(jl.EXPORTED_SYMBOLS)
+    for name, (ret, params) in sigs.items():
+        res_t, arg_ts = jl._SIGNATURES[name]
+        assert len(arg_ts) == len(params), (name, len(arg_ts), len(params))
+        for i, (decl, ct) in enumerate(zip(params, arg_ts)):
+            if "*" in decl:
+                assert ct is ctypes.c_void_p, (name, i, decl)
+            else:
+                assert ct is kinds[decl.replace("const ", "")], (name, i, decl)
+        if "*" in ret:
+            assert res_t is ctypes.c_char_p, name
+        else:
+            assert res_t is kinds[ret], (name, ret)
