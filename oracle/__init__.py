@@ -46,6 +46,8 @@ from .bifocal import (  # noqa: F401
     bifocal_decode_varlen,
     plain_decode_varlen,
     bifocal_prefill_varlen,
+    gather_pages,
+    bifocal_decode_paged,
     sliding_window_attention,
     SCHEDULES,
     seam_group_factor,

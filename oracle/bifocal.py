@@ -41,6 +41,10 @@ Parity pins (see ``tests/test_oracle_*.py``):
   ``bifocal_bruteforce`` on its own rows and prefix, with the cache rows past the
   prefix set to NaN; a sequence with no new rows is skipped; with one sequence
   it equals ``bifocal_three_pass``.
+* ``gather_pages`` / ``bifocal_decode_paged``: a contiguous cache scattered into
+  shuffled pages (by the test, with NaN in every unused page) gathers back exactly,
+  and the paged decode equals ``bifocal_decode_varlen`` / ``plain_decode_varlen``
+  on the contiguous cache.
 * ``sliding_window_attention``: torch's fp64 ``scaled_dot_product_attention`` with an
   explicit band mask; equals pass A of ``bifocal_three_pass``; equals
   ``plain_causal_attention`` when the window covers every key; W = 1 returns v_p.
@@ -74,6 +78,8 @@ __all__ = [
     "bifocal_decode_varlen",
     "plain_decode_varlen",
     "bifocal_prefill_varlen",
+    "gather_pages",
+    "bifocal_decode_paged",
     "sliding_window_attention",
     "SCHEDULES",
     "seam_group_factor",
@@ -625,6 +631,43 @@ def bifocal_prefill_varlen(q, cu_seqlens_q, k_cache, v_cache, seq_lens, pretrain
         out[r0:r1] = o[0]
         lse[:, r0:r1] = l[0]
     return out, lse
+
+
+def gather_pages(pages, block_table, seq_lens):
+    """A paged cache as contiguous per-sequence caches: ``pages [n_pages, page_size,
+    Hkv, D]``, ``block_table [B, pages_per_seq]``; position j of sequence b is row
+    j % page_size of page block_table[b, j // page_size].  Returns ``[B,
+    pages_per_seq * page_size, Hkv, D]`` with NaN past every sequence's length."""
+    pages = np.asarray(pages)
+    bt = np.asarray(block_table, dtype=np.int64)
+    page_size = pages.shape[1]
+    out = np.full((bt.shape[0], bt.shape[1] * page_size) + pages.shape[2:], np.nan)
+    for bi, s in enumerate(int(x) for x in seq_lens):
+        for j in range(s):
+            out[bi, j] = pages[bt[bi, j // page_size], j % page_size]
+    return out
+
+
+def bifocal_decode_paged(q, k_pages, v_pages, block_table, seq_lens, pretrained_window, local_window, rope_base,
+                         softmax_scale=None, schedule="grouped", bifocal=True):
+    """Decode over a paged cache: the cache's pages are only a storage layout, so
+    each sequence is exactly the decode on its gathered prefix (the keys keep their
+    original positions: ResearchPod transcript, cache exchange).  ``q [B, 1, Hq,
+    D]``; returns ``(out [B, 1, Hq, D], lse [B, Hq, 1])``."""
+    k = gather_pages(_as_f64(k_pages), block_table, seq_lens)
+    v = gather_pages(_as_f64(v_pages), block_table, seq_lens)
+    q = _as_f64(q)
+    outs, lses = [], []
+    for bi, s in enumerate(int(x) for x in seq_lens):
+        if bifocal:
+            o, l = bifocal_decode(q[bi:bi + 1], k[bi:bi + 1, :s], v[bi:bi + 1, :s], pretrained_window, local_window,
+                                  rope_base, softmax_scale=softmax_scale, schedule=schedule)
+        else:
+            o, l = plain_causal_attention(q[bi:bi + 1], k[bi:bi + 1, :s], v[bi:bi + 1, :s],
+                                          softmax_scale=softmax_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs, axis=0), np.concatenate(lses, axis=0)
 
 
 def plain_decode_varlen(q, k_cache, v_cache, seq_lens, softmax_scale=None):

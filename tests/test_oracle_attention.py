@@ -480,3 +480,44 @@ def test_explicit_positions_are_rows_of_the_whole_prefill(schedule):
         assert np.abs(op - ref.numpy()).max() <= 1e-12
     with pytest.raises(ValueError):
         oracle.query_positions(3, 10, [0, 4, 10])
+
+
+def test_paged_decode_equals_contiguous():
+    # a contiguous cache scattered row by row into shuffled pages of 8 positions,
+    # every unused page NaN: gathering recovers it, and the paged decode is the
+    # variable-length decode on the contiguous cache
+    big_l, w, base, d, hq, hkv, ps = 8, 3, 1e4, 16, 4, 2, 8
+    lens = [5, 17, 40]
+    n_max = 40
+    pages_per_seq = n_max // ps
+    rng = np.random.default_rng(55)
+    k = np.full((3, n_max, hkv, d), np.nan)
+    v = np.full((3, n_max, hkv, d), np.nan)
+    for bi, s in enumerate(lens):
+        k[bi, :s] = rng.standard_normal((s, hkv, d))
+        v[bi, :s] = rng.standard_normal((s, hkv, d))
+    q = rng.standard_normal((3, 1, hq, d))
+    n_pages = 3 * pages_per_seq + 4
+    perm = rng.permutation(n_pages)
+    table = perm[:3 * pages_per_seq].reshape(3, pages_per_seq)
+    kp = np.full((n_pages, ps, hkv, d), np.nan)
+    vp = np.full((n_pages, ps, hkv, d), np.nan)
+    for bi, s in enumerate(lens):
+        for j in range(s):
+            kp[table[bi, j // ps], j % ps] = k[bi, j]
+            vp[table[bi, j // ps], j % ps] = v[bi, j]
+    kg = oracle.gather_pages(kp, table, lens)
+    for bi, s in enumerate(lens):
+        assert np.array_equal(kg[bi, :s], k[bi, :s]) and np.all(np.isnan(kg[bi, s:]))
+    for sched in oracle.SCHEDULES:
+        o1, l1 = oracle.bifocal_decode_paged(q, kp, vp, table, lens, big_l, w, base, schedule=sched)
+        if sched == "grouped":
+            o2, l2 = oracle.bifocal_decode_varlen(q, k, v, lens, big_l, w, base)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        for bi, s in enumerate(lens):
+            o3, l3 = oracle.bifocal_decode(q[bi:bi + 1], k[bi:bi + 1, :s], v[bi:bi + 1, :s], big_l, w, base,
+                                           schedule=sched)
+            assert np.array_equal(o1[bi:bi + 1], o3) and np.array_equal(l1[bi:bi + 1], l3)
+    op, lp = oracle.bifocal_decode_paged(q, kp, vp, table, lens, big_l, w, base, bifocal=False)
+    o4, l4 = oracle.plain_decode_varlen(q, k, v, lens)
+    assert np.array_equal(op, o4) and np.array_equal(lp, l4)
