@@ -501,6 +501,41 @@ def main():
             log(f"schedule {name} (factor {scheds[name]['factor']:.4g}): prefill {sp_ms:.2f} ms "
                 f"({scheds[name]['prefill_tflops']} TFLOP/s), decode {us:.2f} us")
         result["schedules"] = scheds
+
+        # the same 128K decode over a paged cache: pages of 256 positions in a shuffled order
+        # (each cache copy reshaped to a page pool), bifocal and plain
+        if b == 1:
+            ps = 256
+            n_pages = s // ps
+            perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
+            table = torch.from_numpy(perm).view(1, n_pages).to(dev)
+            sl = torch.tensor([s], dtype=torch.int32, device=dev)
+            pools = [(kc.view(n_pages, ps, hkv, 128), vc.view(n_pages, ps, hkv, 128)) for kc, vc in caches]
+            per = {"bifocal": [], "plain": []}
+            for it in range(args.decode_warmup + args.decode_iters // 2):
+                if it % batch_iters == 0:
+                    torch.cuda._sleep(spin_cycles)
+                for mi, mode in enumerate(("bifocal", "plain")):
+                    kp, vp = pools[(2 * it + mi) % len(pools)]
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if mode == "bifocal":
+                        jl.jl_bifocal_decode_paged(q_dec, kp, vp, out_dec, None, table, sl, big_l, w, base, ws)
+                    else:
+                        jl.jl_plain_decode_paged(q_dec, kp, vp, out_dec, None, table, sl, ws)
+                    e1.record(stream)
+                    if it >= args.decode_warmup:
+                        per[mode].append((e0, e1))
+            torch.cuda.synchronize()
+            kv_bytes = 2 * s * hkv * 128 * 2
+            pg = {"page_size": ps, "n_pages": n_pages, "order": "shuffled"}
+            for mode, lst in per.items():
+                us = float(np.median([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in lst]))
+                pg[mode] = {"us_median": round(us, 2), "GB_s": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
+            pg["overhead_vs_plain"] = round(pg["bifocal"]["us_median"] / pg["plain"]["us_median"] - 1.0, 4)
+            result["decode_paged"] = pg
+            log(f"decode paged (pages of {ps}, shuffled): bifocal {pg['bifocal']['us_median']} us "
+                f"({pg['bifocal']['GB_s']} GB/s), plain {pg['plain']['us_median']} us")
         del caches, slices
 
         # variable-length batched decode: 8 sequences of 16K..128K keys (g = 1..4 within one

@@ -327,6 +327,49 @@ jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void
                                   int32_t n_kv_heads, int32_t head_dim, float softmax_scale,
                                   void* stream);
 
+/* ---- Paged caches ------------------------------------------------------------
+ * Decode over a paged cache: the keys and values of all sequences live in pools of
+ * fixed-size pages, and a table maps each sequence's logical pages to pool pages.
+ * The cache still keeps every key at its original position (ResearchPod
+ * transcript, cache exchange), and g, the seam shift and the fractional rate follow
+ * each sequence's own length (seventnews.com, "How bifocal attention sidesteps the
+ * fixed-scaling trap").
+ *   k_pages/v_pages: bf16 [n_pages, page_size, Hkv, D]; row r of page p holds one
+ *                    position's keys (values) of every KV head
+ *   block_table    : device int32 [B, pages_per_seq], 4-byte aligned: position j of
+ *                    sequence b sits in row j % page_size of page
+ *                    block_table[b * pages_per_seq + j / page_size]
+ *   seq_lens       : device int32 [B]; sequence b holds positions 0 .. s_b-1, 1 <= s_b <=
+ *                    pages_per_seq * page_size, its query at s_b - 1
+ *   page_size      : a power of two in [32, 2^20]
+ *   q, out, lse    : as jl_bifocal_decode_varlen
+ *   workspace      : >= jl_bifocal_decode_workspace_size(B, pages_per_seq * page_size,
+ *                    Hq, Hkv, D) bytes
+ * Device contents are not read on the host: table entries are clamped into the pool
+ * and lengths into range, so values outside the contract give an unspecified result,
+ * never an access outside the pools.  Each sequence gets what jl_bifocal_decode_sched
+ * returns for its contiguous cache, up to rounding order (chunks start at multiples
+ * of the chunk size here, and the chunk holding both remote and local keys turns
+ * its local keys by a zero angle).  Errors as jl_bifocal_decode_varlen, plus
+ * JL_ERR_INVALID_ARG for a NULL or misaligned table or a page_size that is not a
+ * power of two in range. */
+jl_status jl_bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                  void* out, float* lse, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t batch, int32_t n_pages,
+                                  int32_t page_size, int32_t pages_per_seq, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                  int64_t local_window, double rope_base, int32_t schedule,
+                                  float softmax_scale, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Plain decode over a paged cache (same layouts, no correction). */
+jl_status jl_plain_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* out,
+                                float* lse, const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t batch, int32_t n_pages, int32_t page_size,
+                                int32_t pages_per_seq, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, float softmax_scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* ---- Explicit query positions ----------------------------------------------
  * The query rows of a call need not be the newest tokens: row i sits at position
  * q_pos[i] of the n_kv-key context (ResearchPod transcript, cache exchange: the

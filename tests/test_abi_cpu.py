@@ -423,3 +423,38 @@ def test_binding_signatures_match_the_header():
             assert res_t is ctypes.c_char_p, name
         else:
             assert res_t is kinds[ret], (name, ret)
+
+
+def test_paged_decode_validation(lib):
+    need = lib.jl_bifocal_decode_workspace_size(2, 256, 4, 2, 128)
+
+    def bif(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, bt=FAKE, sl=FAKE, batch=2, n_pages=10, ps=64, pps=4,
+                 hq=4, hkv=2, d=128, L=64, w=16, base=1e4, sched=0, scale=0.0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_bifocal_decode_paged(a["q"], a["k"], a["v"], a["out"], a["lse"], a["bt"], a["sl"], a["batch"],
+                                           a["n_pages"], a["ps"], a["pps"], a["hq"], a["hkv"], a["d"], a["L"], a["w"],
+                                           a["base"], a["sched"], a["scale"], a["ws"], a["wsb"], None)
+
+    def plain(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, bt=FAKE, sl=FAKE, batch=2, n_pages=10, ps=64, pps=4,
+                 hq=4, hkv=2, d=128, scale=0.0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.jl_plain_decode_paged(a["q"], a["k"], a["v"], a["out"], a["lse"], a["bt"], a["sl"], a["batch"],
+                                         a["n_pages"], a["ps"], a["pps"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                         a["ws"], a["wsb"], None)
+
+    for call in (bif, plain):
+        assert call(bt=None) == INVALID
+        assert call(bt=FAKE + 2) == INVALID
+        assert call(sl=None) == INVALID
+        assert call(ps=48) == INVALID                  # not a power of two
+        assert call(ps=16) == INVALID                  # below one 32-key block
+        assert call(n_pages=0) == INVALID
+        assert call(pps=0) == INVALID
+        assert call(hq=3) == INVALID
+        assert call(d=64) == UNSUPPORTED
+        assert call(wsb=need - 1) == WORKSPACE
+        if not _has_gpu():
+            assert call() == DEVICE
+    assert bif(sched=1, w=64) == INVALID

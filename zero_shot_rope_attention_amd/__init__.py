@@ -39,6 +39,8 @@ __all__ = [
     "jl_plain_prefill_varlen",
     "jl_bifocal_prefill_positions",
     "jl_plain_prefill_positions",
+    "jl_bifocal_decode_paged",
+    "jl_plain_decode_paged",
     "jl_qwen3_layer_workspace_size",
     "jl_qwen3_attention_layer",
 ]
@@ -83,6 +85,10 @@ _SIGNATURES = {
                                             _i64, _f64, _i32, _f32, _vp, _sz, _vp]),
     "jl_plain_prefill_positions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                           _vp]),
+    "jl_bifocal_decode_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _i64, _i64, _f64, _i32, _f32, _vp, _sz, _vp]),
+    "jl_plain_decode_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _f32, _vp, _sz, _vp]),
     "jl_qwen3_layer_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "jl_qwen3_attention_layer": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _f32, _i32, _i64, _i64, _f64, _i32, _vp, _sz, _vp]),
@@ -380,3 +386,37 @@ def jl_plain_prefill_positions(q, k, v, out, lse, q_pos, softmax_scale=0.0, stre
     _check(load_library().jl_plain_prefill_positions(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                                      _pos_ptr(q_pos), b, n_q, n_kv, hq, hkv, d, float(softmax_scale),
                                                      _stream(stream)))
+
+
+def _table_ptr(t):
+    import torch
+    if t.dtype != torch.int32:
+        raise TypeError("block_table must be an int32 device tensor")
+    return _ptr(t)
+
+
+def jl_bifocal_decode_paged(q, k_pages, v_pages, out, lse, block_table, seq_lens, pretrained_window, local_window,
+                            rope_base, workspace, schedule="grouped", softmax_scale=0.0, stream=None):
+    """q [B, 1, Hq, D]; page pools [n_pages, page_size, Hkv, D]; block_table int32
+    [B, pages_per_seq] and seq_lens int32 [B] on the device; workspace as for
+    jl_bifocal_decode with n_kv = pages_per_seq * page_size."""
+    b, _, hq, d = q.shape
+    n_pages, page_size, hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    pages_per_seq = block_table.shape[1]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_bifocal_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse), _table_ptr(block_table), _seq_lens_ptr(seq_lens),
+        b, n_pages, page_size, pages_per_seq, hq, hkv, d, int(pretrained_window), int(local_window), float(rope_base),
+        _schedule_id(schedule), float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_plain_decode_paged(q, k_pages, v_pages, out, lse, block_table, seq_lens, workspace, softmax_scale=0.0,
+                          stream=None):
+    b, _, hq, d = q.shape
+    n_pages, page_size, hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    pages_per_seq = block_table.shape[1]
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().jl_plain_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse), _table_ptr(block_table), _seq_lens_ptr(seq_lens),
+        b, n_pages, page_size, pages_per_seq, hq, hkv, d, float(softmax_scale), _ptr(workspace), nbytes,
+        _stream(stream)))

@@ -540,6 +540,68 @@ jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v
   return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
 }
 
+static jl_status paged_common(const int32_t* block_table, const int32_t* seq_lens, int32_t n_pages,
+                              int32_t page_size, int32_t pages_per_seq, int32_t n_kv_heads, int32_t* n_kv) {
+  if (!block_table || reinterpret_cast<uintptr_t>(block_table) % 4 != 0)
+    return fail(JL_ERR_INVALID_ARG, "block_table is NULL or not 4-byte aligned");
+  JL_TRY(check_seq_lens(seq_lens));
+  if (page_size < 32 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return fail(JL_ERR_INVALID_ARG, "page_size must be a power of two in [32, 2^20] (got %d)", page_size);
+  if (n_pages < 1 || pages_per_seq < 1)
+    return fail(JL_ERR_INVALID_ARG, "n_pages and pages_per_seq must be >= 1 (got %d, %d)", n_pages, pages_per_seq);
+  const int64_t nkv = (int64_t)pages_per_seq * page_size;
+  if (nkv > 0x7fffffff) return fail(JL_ERR_UNSUPPORTED, "pages_per_seq * page_size exceeds 2^31 - 1");
+  if (elements(n_pages, page_size, n_kv_heads) < 0)
+    return fail(JL_ERR_UNSUPPORTED, "the page pool overflows 64-bit element offsets");
+  *n_kv = (int32_t)nkv;
+  return JL_OK;
+}
+
+jl_status jl_bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* out, float* lse,
+                                  const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                  int32_t n_pages, int32_t page_size, int32_t pages_per_seq, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                  int64_t local_window, double rope_base, int32_t schedule, float softmax_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t n_kv = 0;
+  JL_TRY(paged_common(block_table, seq_lens, n_pages, page_size, pages_per_seq, n_kv_heads, &n_kv));
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_pages, v_pages, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(check_schedule(schedule, pretrained_window, local_window, n_kv));
+  JL_TRY(device_check());
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  jl::DecodeProblem p{q, k_pages, v_pages, out, lse, seq_lens, batch, n_kv, n_q_heads, n_kv_heads,
+                      pretrained_window, w, rope_base, scale, workspace};
+  p.schedule = schedule;
+  p.block_table = block_table;
+  p.pages_per_seq = pages_per_seq;
+  p.page_size = page_size;
+  p.n_pages = n_pages;
+  return launched(jl::launch_decode(true, p, static_cast<hipStream_t>(stream)));
+}
+
+jl_status jl_plain_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* out, float* lse,
+                                const int32_t* block_table, const int32_t* seq_lens, int32_t batch, int32_t n_pages,
+                                int32_t page_size, int32_t pages_per_seq, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, float softmax_scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  int32_t n_kv = 0;
+  JL_TRY(paged_common(block_table, seq_lens, n_pages, page_size, pages_per_seq, n_kv_heads, &n_kv));
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(decode_common(q, k_pages, v_pages, out, lse, s, softmax_scale, &scale, workspace, workspace_bytes));
+  JL_TRY(device_check());
+  jl::DecodeProblem p{q, k_pages, v_pages, out, lse, seq_lens, batch, n_kv, n_q_heads, n_kv_heads, 1, 0, 2.0, scale,
+                      workspace};
+  p.block_table = block_table;
+  p.pages_per_seq = pages_per_seq;
+  p.page_size = page_size;
+  p.n_pages = n_pages;
+  return launched(jl::launch_decode(false, p, static_cast<hipStream_t>(stream)));
+}
+
 // Workspace of the attention layer: projected q/k/v, rotated queries, the
 // attention output, and the attention's own workspace (corrected keys for the
 // prefill, chunk partials for the decode), each 256-byte aligned.

@@ -59,6 +59,12 @@ struct DecodeArgs {
   int32_t sched;       // long-range schedule (Schedule), per sequence
   float scale_log2;
   double theta_rev[kHalfD];
+  // Paged caches (the PAGED kernels only): k and v are pools of n_pages pages of
+  // 2^page_shift positions each ([n_pages, page, Hkv, D]); position j of sequence b
+  // sits in page block_table[b * pages_per_seq + (j >> page_shift)].  n_kv is then
+  // pages_per_seq pages' worth of positions.
+  const int32_t* block_table;
+  int32_t pages_per_seq, page_shift, n_pages;
 };
 
 // How one sequence of s keys is cut: g = g(s) of the schedule for the bifocal
@@ -110,7 +116,12 @@ constexpr int kVmemPerBlock = 16;     // 8 K loads + 8 V copies per block and la
 constexpr int kVBlockBytes = kBlk * 256;
 
 // Two waves per SIMD (<= 256 VGPRs): four workgroups per CU.
-template <bool BIF>
+// PAGED: the cache is a pool of pages (see DecodeArgs).  Chunks then start at
+// multiples of the chunk size rather than at the local window's start, so that
+// every 32-key block lies in one page (pages hold a power of two >= 32
+// positions); the one chunk holding both remote and local keys turns its local
+// keys by a zero angle, which leaves them exactly as cached.
+template <bool BIF, bool PAGED = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
     const DecodeArgs a) {
   // per-wave V blocks, double-buffered; two separate objects so that the
@@ -151,23 +162,51 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int kpg = kWaves * a.kpw;
   const int s_len = seq_length(a.seq_lens, b, a.n_kv);
   const SeqSplit sq = seq_split(s_len, BIF, a.pretrained_window, a.local_window, kpg, a.sliding != 0, a.sched);
-  if (sp >= sq.n_chunks) return;  // a shorter sequence of the batch: no chunk here
   int ks, ke;
   bool remote = false;
-  if (sp < sq.n_rem) {
+  int first_local = 0;  // PAGED: keys from here on take base scores
+  if constexpr (PAGED) {
+    if (sp >= (s_len + kpg - 1) / kpg) return;  // a shorter sequence of the batch: no chunk here
     ks = sp * kpg;
-    ke = min(sq.remote_end, ks + kpg);
-    remote = BIF;
-  } else {
-    ks = sq.remote_end + (sp - sq.n_rem) * kpg;
     ke = min(s_len, ks + kpg);
+    first_local = (BIF && sq.g > 1) ? s_len - min(a.local_window, s_len) : 0;
+    remote = BIF && ks < first_local;
+  } else {
+    if (sp >= sq.n_chunks) return;  // a shorter sequence of the batch: no chunk here
+    if (sp < sq.n_rem) {
+      ks = sp * kpg;
+      ke = min(sq.remote_end, ks + kpg);
+      remote = BIF;
+    } else {
+      ks = sq.remote_end + (sp - sq.n_rem) * kpg;
+      ke = min(s_len, ks + kpg);
+    }
   }
   const int ws = ks + wave * a.kpw;
   const int we = min(ke, ws + a.kpw);
 
   const int64_t kv_rs = (int64_t)a.hkv * kD;
-  const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
-  const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+  const uint16_t* kbase = a.k + (PAGED ? 0 : (int64_t)b * a.n_kv * kv_rs) + (int64_t)kvh * kD;
+  const uint16_t* vbase = a.v + (PAGED ? 0 : (int64_t)b * a.n_kv * kv_rs) + (int64_t)kvh * kD;
+  // PAGED: the pages of this wave's keys (at most 17), one per lane, loaded before
+  // anything else: every block's address needs its page.  Entries are clamped into
+  // the pool (a table outside the contract gives an unspecified result, never an
+  // access out of range).
+  int pt_first = 0, pt_page = 0;
+  if constexpr (PAGED) {
+    pt_first = ws >> a.page_shift;
+    const int idx = min(pt_first + lane, a.pages_per_seq - 1);
+    pt_page = min(max(a.block_table[(int64_t)b * a.pages_per_seq + idx], 0), a.n_pages - 1);
+  }
+  // row of key jb in the cache (PAGED: in the pool)
+  auto cache_row = [&](int jb) -> int64_t {
+    if constexpr (PAGED) {
+      const int pg = __builtin_amdgcn_readlane(pt_page, (jb >> a.page_shift) - pt_first);
+      return ((int64_t)pg << a.page_shift) + (jb & ((1 << a.page_shift) - 1));
+    } else {
+      return jb;
+    }
+  };
 
   // ---- per-block loads: K fragment into registers (key j0 + perm_key(n),
   // d = 16kk + 8h + e), V rows into this wave's LDS buffer by direct copies ----
@@ -183,7 +222,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // the whole wave; readfirstlane states it, or the compiler wraps every buffer
   // load in a loop over the distinct resources it cannot rule out.
   auto rsrc_for = [&](const uint16_t* base, int jb, uint32_t nbytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)jb * kv_rs), (short)0, (int)nbytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + cache_row(jb) * kv_rs), (short)0, (int)nbytes,
+                                             0x00020000);
   };
   auto issue_k = [&](int blk, u32x4 (&kr)[8]) {
     const int j0 = ws + blk * kBlk;
@@ -284,7 +324,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     __builtin_amdgcn_sched_barrier(0);  // nothing that reads the block may move above the wait
     if (BIF && remote) {
       const int t = j0 + perm_key(n) - ws;
-      const float uf = (float)(t - small_div(r_s + t, sq.g, inv_g));
+      // PAGED: a local key of the chunk that holds both kinds turns by zero
+      const float on = (PAGED && (j0 + perm_key(n) >= first_local)) ? 0.0f : 1.0f;
+      const float uf = (float)(t - small_div(r_s + t, sq.g, inv_g)) * on;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const float4 fb0 = *reinterpret_cast<const float4*>(&s_fb[wave][16 * kk + 8 * h]);
@@ -300,7 +342,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             const int e = 2 * e2 + q2;
-            const float rev = fbv[e] - uf * thv[e];  // angle in revolutions
+            const float rev = (PAGED ? fbv[e] * on : fbv[e]) - uf * thv[e];  // angle in revolutions
             const float co = __builtin_amdgcn_cosf(rev);
             const float si = __builtin_amdgcn_sinf(rev);
             const float x1 = elem(kr[kk], e), x2 = elem(kr[kk + 4], e);
@@ -437,7 +479,7 @@ struct CombineArgs {
   uint16_t* out;
   float* lse;
   const int32_t* seq_lens;
-  int32_t n_kv, hq, n_wg, local_window, kpg, bif, sliding, sched;
+  int32_t n_kv, hq, n_wg, local_window, kpg, bif, sliding, sched, paged;
   int64_t pretrained_window;
 };
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const CombineArgs ca) {
@@ -447,8 +489,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const C
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int cl = tid >> 5, c4 = tid & 31;
-  const int n_wg = seq_split(seq_length(ca.seq_lens, (int)(bh / ca.hq), ca.n_kv), ca.bif != 0, ca.pretrained_window,
-                             ca.local_window, ca.kpg, ca.sliding != 0, ca.sched).n_chunks;
+  const int s_len = seq_length(ca.seq_lens, (int)(bh / ca.hq), ca.n_kv);
+  const int n_wg = ca.paged ? (s_len + ca.kpg - 1) / ca.kpg
+                            : seq_split(s_len, ca.bif != 0, ca.pretrained_window, ca.local_window, ca.kpg,
+                                        ca.sliding != 0, ca.sched).n_chunks;
   const float* pl = ca.part_lse + bh * ca.n_wg;  // rows of ca.n_wg slots, the first n_wg filled
   const float* po = ca.part_o + bh * ca.n_wg * kD + 4 * c4;
   uint16_t* out = ca.out;
@@ -572,6 +616,18 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   a.seq_lens = p.seq_lens;
   a.sliding = p.sliding ? 1 : 0;
   if (p.sliding && bifocal) return hipErrorInvalidValue;
+  const bool paged = p.block_table != nullptr;
+  a.block_table = p.block_table;
+  a.pages_per_seq = p.pages_per_seq;
+  a.n_pages = p.n_pages;
+  a.page_shift = 0;
+  if (paged) {
+    // pages of a power of two >= 32 positions, lengths per sequence, no window-only mode
+    if (p.sliding || !p.seq_lens || p.page_size < kBlk || (p.page_size & (p.page_size - 1)) != 0 || p.n_pages < 1 ||
+        (int64_t)p.pages_per_seq * p.page_size != p.n_kv)
+      return hipErrorInvalidValue;
+    while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
+  }
   a.pretrained_window = bifocal ? p.pretrained_window : 1;
   a.local_window = (bifocal || p.sliding) ? p.local_window : 0;
   a.sched = bifocal ? p.schedule : kSchedGrouped;
@@ -585,8 +641,12 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   }
   a.kpw = kBlk * a.nb;
   const int32_t chunk = kWaves * a.kpw;
-  if (p.seq_lens) {
-    a.n_wg = decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);  // any length up to n_kv fits
+  if (paged) {
+    // chunks start at multiples of the chunk: at most ceil(n_kv / chunk) per sequence
+    a.n_wg = (p.n_kv + chunk - 1) / chunk;
+  } else if (p.seq_lens) {
+    // any length up to n_kv fits (the cut at the local window's start may add one chunk)
+    a.n_wg = decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);
   } else if (p.sliding) {
     const int32_t w = p.local_window < p.n_kv ? p.local_window : p.n_kv;
     a.n_wg = (w + chunk - 1) / chunk;
@@ -618,7 +678,11 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   const int ncu = device_cu_count();
   a.order_ncu = (ncu > 0 && n_bh % kOrderHeads == 0 && n_grid % ((int64_t)ncu * kOrderHeads) == 0) ? ncu : 0;
   if (n_grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (bifocal)
+  if (paged && bifocal)
+    hipLaunchKernelGGL((decode_split_kernel<true, true>), dim3((unsigned)n_grid), dim3(kWaves * 64), 0, stream, a);
+  else if (paged)
+    hipLaunchKernelGGL((decode_split_kernel<false, true>), dim3((unsigned)n_grid), dim3(kWaves * 64), 0, stream, a);
+  else if (bifocal)
     hipLaunchKernelGGL((decode_split_kernel<true>), dim3((unsigned)n_grid), dim3(kWaves * 64), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_split_kernel<false>), dim3((unsigned)n_grid), dim3(kWaves * 64), 0, stream, a);
@@ -638,6 +702,7 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
   ca.bif = bifocal ? 1 : 0;
   ca.sliding = a.sliding;
   ca.sched = a.sched;
+  ca.paged = paged ? 1 : 0;
   ca.pretrained_window = a.pretrained_window;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kCombineThreads), 0, stream, ca);
   return hipGetLastError();

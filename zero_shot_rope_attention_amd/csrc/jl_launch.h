@@ -106,6 +106,11 @@ struct DecodeProblem {
   void* workspace;
   bool sliding = false;  // plain attention over the newest min(W, s) keys only (bifocal must be false)
   int32_t schedule = kSchedGrouped;  // long-range schedule, taken per sequence in the kernels
+  // Paged cache: k and v are pools [n_pages, page_size, Hkv, D]; position j of
+  // sequence b in page block_table[b * pages_per_seq + j / page_size] (device);
+  // page_size a power of two >= 32, n_kv = pages_per_seq * page_size, seq_lens set.
+  const int32_t* block_table = nullptr;
+  int32_t pages_per_seq = 0, page_size = 0, n_pages = 0;
 };
 
 // Number of key chunks the decode splits a cache of n_kv keys into (upper bound
