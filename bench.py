@@ -114,7 +114,8 @@ def cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, n_rows, seed=0):
             "kind": "oracle",
             "sample": f"{n_rows} random query rows x {grp} query heads (KV head 0) of the workload, "
                       f"fp64 numpy three-pass oracle, {dt:.1f} s; rate = algorithmic flops of those rows / time",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+            "seconds": dt, "host_cpus": os.cpu_count(),
+            "pairs_per_s": grp * float(np.sum(rows + 1)) / dt}
 
 
 def bench_prefill_varlen(jl, torch, s, hq, hkv, big_l, w, base, args):
@@ -243,8 +244,8 @@ def bench_layer(jl, torch, s, hq, hkv, big_l, w, base, args, result):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-iters", type=int, default=200, help="timed decode calls per mode and length")
     ap.add_argument("--decode-warmup", type=int, default=20)
@@ -345,6 +346,7 @@ def main():
                      "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3, false>: rocprofv3 FETCH_SIZE x 2.0 + "
                                      "WRITE_SIZE x 1.0 (scales from a 1 GiB copy), null if the kernel changed since"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
+        "prefill_pairs_per_s": b * hq * s * (s + 1) / 2 / (pre_avg * 1e-3),
         "decode_in_step_us": round(float(np.mean(dec_ms)) * 1e3, 2),
     }
 
