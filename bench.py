@@ -249,7 +249,7 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--decode-iters", type=int, default=200, help="timed decode calls per mode and length")
     ap.add_argument("--decode-warmup", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the plain-prefill and decode comparisons")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -362,7 +362,7 @@ def main():
         torch.cuda.synchronize()
         fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
         result["fused_prefill"] = {"ms": round(fused_ms, 4), "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
-                                   "kernel": "prefill_pp_kernel<1>", "over_two_launch_time": round(fused_ms / pre_avg, 4)}
+                                   "kernel": "prefill_pp_kernel<1, false>", "over_two_launch_time": round(fused_ms / pre_avg, 4)}
         log(f"single-kernel bifocal prefill {fused_ms:.2f} ms")
 
         # plain causal prefill built the same way (same numerator)
@@ -410,7 +410,7 @@ def main():
         result["sliding_window"] = {
             "window": w,
             "prefill": {"ms": round(sl_ms, 4), "tflops": round(sl_flops / (sl_ms * 1e-3) / 1e12, 2),
-                        "flops": sl_flops, "kernel": "prefill_pp_kernel<4>"},
+                        "flops": sl_flops, "kernel": "prefill_pp_kernel<4, false>"},
             "decode": {"us_median": round(sd_us, 2), "kv_bytes": 2 * b * min(w, s) * hkv * 128 * 2},
         }
         log(f"sliding window W={w}: prefill {sl_ms:.2f} ms ({sl_flops / (sl_ms * 1e-3) / 1e12:.1f} TFLOP/s), "
