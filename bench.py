@@ -340,10 +340,10 @@ def main():
                    "group_factor": g},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "prefill_pp_kernel<3, false> (bifocal, corrected keys staged) + correct_keys_kernel<false>",
+                     "kernel": "prefill_pp_kernel<3, false, false> (bifocal, corrected keys staged) + correct_keys_kernel<false>",
                      "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
                      "timing": "HIP events around the whole prefill call (both launches) on its stream",
-                     "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3, false>: rocprofv3 FETCH_SIZE x 2.0 + "
+                     "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3, false, false>: rocprofv3 FETCH_SIZE x 2.0 + "
                                      "WRITE_SIZE x 1.0 (scales from a 1 GiB copy), null if the kernel changed since"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
         "prefill_pairs_per_s": b * hq * s * (s + 1) / 2 / (pre_avg * 1e-3),
@@ -362,7 +362,7 @@ def main():
         torch.cuda.synchronize()
         fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
         result["fused_prefill"] = {"ms": round(fused_ms, 4), "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
-                                   "kernel": "prefill_pp_kernel<1, false>", "over_two_launch_time": round(fused_ms / pre_avg, 4)}
+                                   "kernel": "prefill_pp_kernel<1, false, false>", "over_two_launch_time": round(fused_ms / pre_avg, 4)}
         log(f"single-kernel bifocal prefill {fused_ms:.2f} ms")
 
         # plain causal prefill built the same way (same numerator)
@@ -410,7 +410,7 @@ def main():
         result["sliding_window"] = {
             "window": w,
             "prefill": {"ms": round(sl_ms, 4), "tflops": round(sl_flops / (sl_ms * 1e-3) / 1e12, 2),
-                        "flops": sl_flops, "kernel": "prefill_pp_kernel<4, false>"},
+                        "flops": sl_flops, "kernel": "prefill_pp_kernel<4, false, false>"},
             "decode": {"us_median": round(sd_us, 2), "kv_bytes": 2 * b * min(w, s) * hkv * 128 * 2},
         }
         log(f"sliding window W={w}: prefill {sl_ms:.2f} ms ({sl_flops / (sl_ms * 1e-3) / 1e12:.1f} TFLOP/s), "
