@@ -111,3 +111,15 @@ def test_paged_decode_128k_qwen3_shape():
     ro, rl = _oracle(qb, kp, vp, table, lens, 32768, 4096, 1e6)
     assert_parity(out, ro)
     assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+
+
+def test_paged_decode_wave_without_keys():
+    # 131072 - 600 keys: the last chunk (1024 keys per chunk, 512 per wave here) holds 424,
+    # so its second wave has no keys and re-reads the chunk's last key, which sits in an
+    # earlier page than the wave's own start
+    lens = (131072 - 600, 70001)
+    qb, kp, vp, table = _paged_inputs(1040, list(lens), 32, 8, 256, spare_pages=2)
+    out, lse = _run(qb, kp, vp, table, lens, 32768, 4096, 1e6)
+    ro, rl = _oracle(qb, kp, vp, table, lens, 32768, 4096, 1e6)
+    assert_parity(out, ro)
+    assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)

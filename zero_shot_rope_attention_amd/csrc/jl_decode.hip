@@ -201,7 +201,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // row of key jb in the cache (PAGED: in the pool)
   auto cache_row = [&](int jb) -> int64_t {
     if constexpr (PAGED) {
-      const int pg = __builtin_amdgcn_readlane(pt_page, (jb >> a.page_shift) - pt_first);
+      // a wave with no keys of its own re-reads the chunk's last key, which may sit in
+      // an earlier page than the wave's start: clamp the lane index into the table
+      const int pg = __builtin_amdgcn_readlane(pt_page, max((jb >> a.page_shift) - pt_first, 0));
       return ((int64_t)pg << a.page_shift) + (jb & ((1 << a.page_shift) - 1));
     } else {
       return jb;
