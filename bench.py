@@ -184,7 +184,8 @@ def bench_layer(jl, torch, s, hq, hkv, big_l, w, base, args, result):
     ws = torch.empty(jl.jl_qwen3_layer_workspace_size(1, s, s, hq, hkv), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     res = {"shape": {"hidden": hidden, "q_heads": hq, "kv_heads": hkv, "head_dim": 128, "seq_len": s},
-           "data": "seeded device normals; projections by rocBLAS"}
+           "data": "seeded device normals; prefill projections by rocBLAS, a decode step's by the library's "
+                   "weight-streaming kernel"}
 
     def prefill(bif):
         jl.jl_qwen3_attention_layer(x, w_qkv, gq, gk, w_o, out, kc, vc, ws, bifocal=bif, pretrained_window=big_l,

@@ -100,6 +100,8 @@ CASES = [
     (502, 1, (640,), 256, 4, 4, False, 1, 1, 1e4, "grouped"),             # the plain layer
     (503, 1, (500, 1), 256, 4, 2, True, 128, 32, 1e4, "seam"),
     (504, 1, (500, 1), 256, 4, 2, True, 128, 32, 1e4, "fractional"),
+    (507, 5, (200, 1), 256, 4, 2, True, 128, 32, 1e4, "grouped"),      # a decode step of 5 tokens
+    (508, 9, (300, 1), 256, 4, 2, True, 128, 32, 1e4, "seam"),        # 9 tokens: past the few-token kernel
 ]
 
 

@@ -1,6 +1,7 @@
 // Pieces of a Qwen3-shaped attention layer around the attention kernels: the
 // per-head RMSNorm + RoPE + cache append that turns the projected q/k/v into the
-// attention's inputs, and the projections themselves (rocBLAS bf16 GEMMs).
+// attention's inputs, and the projections themselves (rocBLAS bf16 GEMMs, and a
+// weight-streaming kernel of our own for the few tokens of a decode step).
 //
 // The method runs inside Qwen3 models (seventnews.com, "Empirical results that
 // challenge the status quo"); a layer of them projects the hidden states to
@@ -88,6 +89,84 @@ __global__ __launch_bounds__(kNormThreads) void norm_rope_kernel(const NormRopeA
   *reinterpret_cast<u32x2*>(dst + kHalfD + 4 * l) = o_hi;
 }
 
+// y[t, r] = sum_k x[t, k] w[r, k] for a handful of tokens (a decode step): the
+// product reads every weight once, so it is bound by the weight bytes, and a
+// wave per kGemvRows output rows streams them with 16-byte loads while every
+// lane keeps the tokens' matching 8 elements beside them.  Dot products of bf16
+// pairs accumulate in fp32 (v_dot2), then a 64-lane reduction per output.
+constexpr int kGemvMaxTokens = 8;
+constexpr int kGemvRows = 4;
+constexpr int kGemvWaves = 4;
+
+template <int T>
+__global__ __launch_bounds__(kGemvWaves * 64) void gemv_xwt_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ w,
+                                                                    uint16_t* __restrict__ y, int n, int k) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * kGemvWaves + wave) * kGemvRows;
+  if (row0 >= n) return;  // whole waves leave together
+  const uint16_t* wr[kGemvRows];
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r) wr[r] = w + (int64_t)min(row0 + r, n - 1) * k;
+  float acc[kGemvRows][T];
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[r][t] = 0.0f;
+#pragma unroll 2
+  for (int k0 = 8 * lane; k0 < k; k0 += 512) {
+    u32x4 wv[kGemvRows], xv[T];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) wv[r] = *reinterpret_cast<const u32x4*>(wr[r] + k0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) xv[t] = *reinterpret_cast<const u32x4*>(x + (int64_t)t * k + k0);
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // each element is copied out first: bit_cast of a vector element in place
+          // reads element 0 whatever the index (hipcc's front end)
+          const uint32_t wp = wv[r][e], xp = xv[t][e];
+          acc[r][t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp), __builtin_bit_cast(bf16x2, xp),
+                                                      acc[r][t], false);
+        }
+  }
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float v = acc[r][t];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      acc[r][t] = v;
+    }
+  if (lane < T) {
+    // lane t writes token t's rows
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      if (t == lane)
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r)
+          if (row0 + r < n) {
+            const uint32_t pk = pack_bf16(acc[r][t], 0.0f);
+            y[(int64_t)t * n + row0 + r] = (uint16_t)(pk & 0xffffu);
+          }
+  }
+}
+
+template <int T>
+hipError_t launch_gemv(const void* x, const void* w, void* y, int n, int k, hipStream_t stream) {
+  const int per_block = kGemvRows * kGemvWaves;
+  const int blocks = (n + per_block - 1) / per_block;
+  hipLaunchKernelGGL((gemv_xwt_kernel<T>), dim3(blocks), dim3(kGemvWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), static_cast<uint16_t*>(y), n,
+                     k);
+  return hipGetLastError();
+}
+
 // rocBLAS handle of the calling thread for the current device (created on
 // first use and kept until the process ends).
 rocblas_handle thread_handle() {
@@ -131,6 +210,20 @@ hipError_t launch_gemm_xwt(const void* x, const void* w, void* y, int64_t m, int
                            hipStream_t stream) {
   if (m == 0) return hipSuccess;
   if (m > 0x7fffffff || n > 0x7fffffff || k > 0x7fffffff) return hipErrorInvalidValue;
+  // a few tokens (decode): the weight-streaming kernel above; 16-byte rows need k % 8 == 0
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) % 16 == 0 && k % 8 == 0;
+  if (m <= kGemvMaxTokens && aligned) {
+    switch (m) {
+      case 1: return launch_gemv<1>(x, w, y, (int)n, (int)k, stream);
+      case 2: return launch_gemv<2>(x, w, y, (int)n, (int)k, stream);
+      case 3: return launch_gemv<3>(x, w, y, (int)n, (int)k, stream);
+      case 4: return launch_gemv<4>(x, w, y, (int)n, (int)k, stream);
+      case 5: return launch_gemv<5>(x, w, y, (int)n, (int)k, stream);
+      case 6: return launch_gemv<6>(x, w, y, (int)n, (int)k, stream);
+      case 7: return launch_gemv<7>(x, w, y, (int)n, (int)k, stream);
+      default: return launch_gemv<8>(x, w, y, (int)n, (int)k, stream);
+    }
+  }
   rocblas_handle h = thread_handle();
   if (!h) return hipErrorInvalidValue;
   if (rocblas_set_stream(h, stream) != rocblas_status_success) return hipErrorInvalidValue;
