@@ -1049,10 +1049,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   // One tile of the ping-pong program: phase M(k), barrier, phase V(k), barrier.
   // Tile kinds: kInterior (all keys causal and, bifocal, remote for every row
   // of the workgroup: grouped scores, no masks), kEdge (bifocal: keys local for
-  // some rows and remote for others: both score kinds) and kLocal (every causal
+  // some rows and remote for others: both score kinds), kLocalFree (precorrected
+  // bifocal and sliding window: every key causal and local for every row: base
+  // scores, no masks, the interior tiles' interleaved MFMA phase) and kLocal (every causal
   // key local for every row: base scores with the causal mask).  Only the one
   // or two edge tiles of a sweep keep both query fragments live.
-  constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
+  constexpr int kInterior = 0, kEdge = 1, kLocal = 2, kLocalFree = 3;
   auto tile = [&](int k, auto kind_tag) {
     constexpr int kKind = decltype(kind_tag)::value;
     // the wave in its MFMA phase goes first when both waves of a SIMD can issue
@@ -1069,9 +1071,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // V of tile k-1 (at the first tile the probabilities are zero and that
     // tile's finite V is read instead, which adds exactly nothing)
     const uint8_t* svp = s_v + ((k > t0 ? k - 1 : t0) % 3) * kTileBytes;
-    if constexpr (kKind == kInterior) {
+    if constexpr (kKind == kInterior || kKind == kLocalFree) {
+      constexpr bool kG = kGrouped && kKind == kInterior;  // grouped scores on remote tiles only
       f32x16 sc[2];
-      mphase_interior<true>(kGrouped ? skg : sk, svp, lofs, kGrouped ? qg : qf, pk, sc, acc);
+      mphase_interior<true>(kG ? skg : sk, svp, lofs, kG ? qg : qf, pk, sc, acc);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1105,20 +1108,20 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     }
     if (kRotate && do_stage) load_half(regs, kbase, vbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
     // ---- V(k): softmax of tile k, staging ----
-    if (kKind == kInterior || uses(k)) {
+    if (kKind == kInterior || kKind == kLocalFree || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
       softmax_exp<1>(xs, m_run, l_run, a.scale_log2, pk);
     }
     // the scores are dead once the probabilities exist: keep the staging after
     __builtin_amdgcn_sched_barrier(0);
     if (do_stage) {
-      if constexpr (kKind == kLocal)  // every later tile is local: no corrected keys needed
+      if constexpr (kKind == kLocal || kKind == kLocalFree)  // every later tile is local: no corrected keys
         store_half<false>(regs, s_k + (tt & 1) * kTileBytes, nullptr, s_v + (tt % 3) * kTileBytes, nullptr,
                           nullptr, 0, 1, 1.0f, grp, gtid);
       else
         store(tt, 2 * grp + (k & 1));
     }
-    if constexpr (kRotate && kKind != kLocal) {
+    if constexpr (kRotate && kKind != kLocal && kKind != kLocalFree) {
       // base of the tile this group stages in V(k+1), into the other slot
       if (gtid < 64) base_angles(tt + 1, 2 * grp + ((k + 1) & 1));
     }
@@ -1137,6 +1140,21 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   }
   if constexpr (kGrouped || kSliding)
     for (; k < t_local; ++k) tile(k, std::integral_constant<int, kEdge>{});
+  if constexpr (kPre || kSliding) {
+    // local tiles below the workgroup's first row need no mask, as in plain mode
+    // (not in the fused bifocal kernel, whose interior loop has no registers to spare)
+    const int t_free = min(ntiles, max(k, (p0_wg + 1) / kBN));
+    if constexpr (kPre) {
+      // the base query fragment afresh: the copy from before the edge tiles, where
+      // both fragments are live, is partly held in scratch by then
+      const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+      asm volatile("" : "+v"(qrow));
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+    }
+    for (; k < t_free; ++k) tile(k, std::integral_constant<int, kLocalFree>{});
+  }
   for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{});
   if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lofs, pk, acc);
   if (grp == 0) __syncthreads();
