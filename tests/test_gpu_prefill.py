@@ -46,6 +46,7 @@ CASES = [
     (106, 1, 513, 513, 4, 4, 512, 64, 1e6),       # s = L + 1 -> g = 2
     (107, 1, 1, 333, 4, 2, 100, 7, 1e4),          # one query row (decode-shaped prefill)
     (108, 1, 1000, 1000, 16, 4, 128, 128, 1e6),   # G = 4 with 4 KV heads, g = 8
+    (109, 1, 1500, 1500, 4, 2, 600, 520, 1e4),    # wide window: up to 7 unmasked local tiles per block, g = 3
 ]
 
 

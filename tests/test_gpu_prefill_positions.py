@@ -47,6 +47,7 @@ CASES = [
     (700, 1, 1000, 300, 4, 2, 256, 64, 1e4),     # g = 4; gaps and repeats
     (701, 2, 700, 97, 8, 2, 128, 100, 1e6),      # batch 2, W close to L
     (702, 1, 2048, 64, 4, 4, 512, 128, 1e4),     # one query block spread over the whole context
+    (703, 1, 1500, 400, 4, 2, 600, 520, 1e4),    # wide window: unmasked local tiles below each block's rows
 ]
 
 

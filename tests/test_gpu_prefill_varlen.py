@@ -67,6 +67,7 @@ CASES = [
     (601, [(64, 64), (0, 100), (129, 700), (200, 200)], 4, 4, 128, 128, 1e6),    # an empty chunk; W = L
     (602, [(700, 700), (33, 2000)], 16, 2, 512, 100, 1e4),                        # G = 8
     (603, [(50, 50), (400, 400)], 4, 2, 512, 64, 1e4),                            # every s_b <= L: g = 1
+    (604, [(900, 900), (257, 1500)], 4, 2, 600, 520, 1e4),                       # wide window, g = 2, 3
 ]
 
 

@@ -45,6 +45,7 @@ CASES = [
     (404, 1, 700, 700, 8, 1, 64),       # a window of exactly one tile
     (405, 1, 513, 513, 4, 4, 65),       # one key past a tile
     (406, 1, 1000, 1000, 16, 4, 256),
+    (407, 1, 1500, 1500, 4, 2, 700),    # wide window: many tiles inside every row's window, unmasked
 ]
 
 
