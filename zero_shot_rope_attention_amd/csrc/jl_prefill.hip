@@ -1097,10 +1097,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     __builtin_amdgcn_s_setprio(0);
     // the row maxima belong to this phase: left to itself the compiler hoists
     // them above the barrier, where the MFMA wave would first wait for its last
-    // products instead of reaching the barrier as soon as they are issued (not
-    // in the precorrected kernel, whose staging registers stay live across the
-    // MFMA phase: there the longer live range costs spills in the loop)
-    if constexpr (!kPre) {
+    // products instead of reaching the barrier as soon as they are issued
+    {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
