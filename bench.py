@@ -2,27 +2,26 @@
 """Benchmark of the bifocal-attention hot path on one MI355X.
 
 A step is one pass of the whole path over one synthetic batch: the bifocal
-prefill of the prompt (g(s), the correction rotation, the three-pass merge) --
-timed in its two-launch form, an elementwise pass that writes the corrected keys
-to a workspace followed by the attention kernel -- then one bifocal decode step
-of the next token against the resulting cache (split-K kernel + combine).  The
-single-kernel form, which corrects every key tile inside the attention kernel,
-is timed next to it.  The default workload is the
-Qwen3-8B-shaped attention layer at 128K: batch 1, 32 query / 8 KV heads,
-head_dim 128, seq 131072, pretrained window 32768, local window 4096, RoPE base
-1e6 (g = 4), bf16 N(0,1) inputs from a fixed seed.
+prefill of the prompt (g(s), the correction rotation, the three-pass merge) in
+its single-kernel form -- every key tile corrected in LDS inside the attention
+kernel, no corrected copy stored -- then one bifocal decode step of the next
+token against the resulting cache (split-K kernel + combine).  The default
+workload is the Qwen3-8B-shaped attention layer at 128K: batch 1, 32 query / 8
+KV heads, head_dim 128, seq 131072, pretrained window 32768, local window 4096,
+RoPE base 1e6 (g = 4), bf16 N(0,1) inputs from a fixed seed.
 
 Printed (one JSON line): prefill TFLOP/s on the algorithmic count
 4*D*Hq*B*s(s+1)/2 as ``value``; the roofline of the prefill kernel (bf16 MFMA
-peak 2.5 PFLOP/s); decode HBM GB/s over the K+V bytes at caches of 32K, 64K
-and 128K positions (cache slices rotated so the 256 MB last-level cache cannot
-hold them) and its overhead vs the plain decode built the same way; the plain
-causal prefill for comparison; the sliding-window layers of hybrid models; a
-batch of 8 sequences of different lengths; the prefill and decode under each
-long-range schedule (integer grouping, seam-shifted grouping, fractional
-scaling); one Qwen3-8B-shaped attention layer (projections, norm, RoPE,
-attention) with the bifocal and with plain attention; and the fp64 CPU oracle
-timed on a bounded sample of rows.
+peak 2.5 PFLOP/s); the two-launch prefill (corrected keys written to a
+workspace first: a deviation from the method, for comparison); the plain causal
+prefill built the same way; the 64K Qwen3-1.7B-shaped prefill and the length
+sweep 4K..128K in all three forms; decode HBM GB/s over the K+V bytes at caches
+of 32K, 64K and 128K positions (cache slices rotated so the 256 MB last-level
+cache cannot hold them) and its overhead vs the plain decode; the
+sliding-window layers of hybrid models; a batch of 8 sequences of different
+lengths; the prefill and decode under each long-range schedule; one
+Qwen3-8B-shaped attention layer with the bifocal and with plain attention; and
+the fp64 CPU oracle timed on a bounded sample of rows.
 """
 
 from __future__ import annotations
@@ -43,6 +42,7 @@ METRIC = "bifocal prefill TFLOP/s @128K (% MFMA peak) + decode GB/s and overhead
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 DECODE_LENGTHS = (32768, 65536, 131072)
+SWEEP_LENGTHS = (4096, 16384, 32768, 49152, 98304, 131072)
 
 WORKLOADS = {
     # name: (workload id, batch, seq, Hq, Hkv, L, W, base)
@@ -53,7 +53,8 @@ WORKLOADS = {
 }
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bifocal_qwen3_8b_128k_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bifocal_fused_qwen3_8b_128k_hbm_traffic.md")
+ROOFLINE_KERNEL = "prefill_pp_kernel<1, false, false>"
 
 
 def measured_traffic():
@@ -83,6 +84,40 @@ def measured_traffic():
         except OSError:
             return None
     return value
+
+
+def time_prefill(torch, stream, call, warmup=3, runs=10):
+    """Average and minimum ms of `call` (one prefill) over `runs` timed calls after
+    `warmup` untimed ones, HIP events on the library's stream."""
+    for _ in range(warmup):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(runs)]
+    for e in ev:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    return float(np.mean(ms)), float(min(ms))
+
+
+def prefill_forms(jl, torch, stream, q, k, v, big_l, w, base, ws, flops):
+    """The three prefill forms on one problem: ms, TFLOP/s and fraction of the bf16 peak."""
+    out = torch.empty_like(q)
+    res = {}
+    calls = {
+        "fused": lambda: jl.jl_bifocal_prefill(q, k, v, out, None, big_l, w, base),
+        "two_launch": lambda: jl.jl_bifocal_prefill_ws(q, k, v, out, None, big_l, w, base, ws),
+        "plain": lambda: jl.jl_plain_prefill(q, k, v, out, None),
+    }
+    for name, call in calls.items():
+        avg, mn = time_prefill(torch, stream, call)
+        tf = flops / (avg * 1e-3) / 1e12
+        res[name] = {"ms": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(tf, 2),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    res["fused_over_plain_time"] = round(res["fused"]["ms"] / res["plain"]["ms"], 4)
+    del out
+    return res
 
 
 def log(msg):
@@ -298,7 +333,7 @@ def main():
 
     def step(ev):
         ev[0].record(stream)
-        jl.jl_bifocal_prefill_ws(q, k, v, out, lse, big_l, w, base, ws_pre)
+        jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
         ev[1].record(stream)
         jl.jl_bifocal_decode(q_dec, k, v, out_dec, None, big_l, w, base, ws)
         ev[2].record(stream)
@@ -341,10 +376,10 @@ def main():
                    "group_factor": g},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "prefill_pp_kernel<3, false, false> (bifocal, corrected keys staged) + correct_keys_kernel<false>",
+                     "kernel": ROOFLINE_KERNEL + " (bifocal prefill, keys corrected tile by tile in LDS)",
                      "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
-                     "timing": "HIP events around the whole prefill call (both launches) on its stream",
-                     "traffic_note": "HBM bytes per launch of prefill_pp_kernel<3, false, false>: rocprofv3 FETCH_SIZE x 2.0 + "
+                     "timing": "HIP events around the single-launch prefill call on its stream",
+                     "traffic_note": "HBM bytes per launch of " + ROOFLINE_KERNEL + ": rocprofv3 FETCH_SIZE x 2.0 + "
                                      "WRITE_SIZE x 1.0 (scales from a 1 GiB copy), null if the kernel changed since"},
         "prefill_ms": {"avg": round(pre_avg, 4), "min": round(min(pre_ms), 4)},
         "prefill_pairs_per_s": b * hq * s * (s + 1) / 2 / (pre_avg * 1e-3),
@@ -352,36 +387,59 @@ def main():
     }
 
     if not args.no_extras:
-        # single-kernel bifocal prefill (keys corrected tile by tile in the kernel)
-        for _ in range(2):
-            jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for e in ev:
-            e[0].record(stream)
-            jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        result["fused_prefill"] = {"ms": round(fused_ms, 4), "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
-                                   "kernel": "prefill_pp_kernel<1, false, false>", "over_two_launch_time": round(fused_ms / pre_avg, 4)}
-        log(f"single-kernel bifocal prefill {fused_ms:.2f} ms")
+        # two-launch bifocal prefill: corrected keys written to a workspace by a pass of their own,
+        # then staged like plain keys (a deviation from the method's single kernel, for comparison)
+        ws_avg, ws_min = time_prefill(torch, stream, lambda: jl.jl_bifocal_prefill_ws(q, k, v, out, lse, big_l, w,
+                                                                                        base, ws_pre), runs=args.steps)
+        result["two_launch_prefill"] = {
+            "ms": round(ws_avg, 4), "ms_min": round(ws_min, 4), "tflops": round(flops / (ws_avg * 1e-3) / 1e12, 2),
+            "frac": round(flops / (ws_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": "correct_keys_kernel<false> + prefill_pp_kernel<3, false, false>",
+            "note": "stores a corrected copy of the keys in a caller workspace for the call; not the method's form"}
+        log(f"two-launch bifocal prefill {ws_avg:.2f} ms")
 
         # plain causal prefill built the same way (same numerator)
         out_p = torch.empty_like(q)
-        for _ in range(2):
-            jl.jl_plain_prefill(q, k, v, out_p, None)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for e in ev:
-            e[0].record(stream)
-            jl.jl_plain_prefill(q, k, v, out_p, None)
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        plain_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        result["plain_prefill"] = {"ms": round(plain_ms, 4),
+        plain_ms, plain_min = time_prefill(torch, stream, lambda: jl.jl_plain_prefill(q, k, v, out_p, None),
+                                           runs=args.steps)
+        result["plain_prefill"] = {"ms": round(plain_ms, 4), "ms_min": round(plain_min, 4),
                                    "tflops": round(flops / (plain_ms * 1e-3) / 1e12, 2),
+                                   "frac": round(flops / (plain_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                    "bifocal_over_plain_time": round(pre_avg / plain_ms, 4)}
         log(f"plain prefill {plain_ms:.2f} ms")
         del out_p
+
+        # length sweep (32 query / 8 KV heads, L = 32768): prefixes of the workload's tensors
+        if b == 1 and hq == 32 and hkv == 8:
+            sweep_p = []
+            for n in SWEEP_LENGTHS:
+                if n > s:
+                    continue
+                qs, ks, vs = q[:, :n], k[:, :n], v[:, :n]
+                fl = prefill_flops(1, n, hq)
+                r = {"seq_len": n, "g": jl.jl_group_factor(n, big_l), "flops": fl}
+                r.update(prefill_forms(jl, torch, stream, qs, ks, vs, big_l, w, base, ws_pre, fl))
+                sweep_p.append(r)
+                log(f"prefill sweep {n} (g={r['g']}): fused {r['fused']['ms']} ms ({r['fused']['frac']}), "
+                    f"two-launch {r['two_launch']['ms']} ms, plain {r['plain']['ms']} ms")
+            result["prefill_sweep"] = sweep_p
+
+        # the Qwen3-1.7B-shaped prefill: 16 query / 8 KV heads at 64K (g = 2), seeded device normals
+        if s >= 65536:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(1717)
+            n17, hq17 = 65536, 16
+            q17 = torch.randn(1, n17, hq17, 128, generator=gen, device=dev).to(torch.bfloat16)
+            k17 = torch.randn(1, n17, hkv, 128, generator=gen, device=dev).to(torch.bfloat16)
+            v17 = torch.randn(1, n17, hkv, 128, generator=gen, device=dev).to(torch.bfloat16)
+            fl = prefill_flops(1, n17, hq17)
+            r = {"workload": "qwen3_1p7b_64k", "seq_len": n17, "q_heads": hq17, "kv_heads": hkv,
+                 "g": jl.jl_group_factor(n17, big_l), "flops": fl, "data": "seeded device normals"}
+            r.update(prefill_forms(jl, torch, stream, q17, k17, v17, big_l, w, base, ws_pre, fl))
+            result["prefill_qwen3_1p7b_64k"] = r
+            log(f"prefill qwen3-1.7B 64K: fused {r['fused']['ms']} ms ({r['fused']['frac']}), "
+                f"two-launch {r['two_launch']['ms']} ms, plain {r['plain']['ms']} ms")
+            del q17, k17, v17
 
         # sliding-window layers of a hybrid model (window W, base RoPE): prefill and decode at this length;
         # algorithmic work 4*D*Hq*B*sum_i min(p_i + 1, W)
@@ -472,14 +530,14 @@ def main():
         result["decode_sweep"] = sweep
 
         # long-range schedules (integer grouping, seam-shifted grouping, fractional scaling): the
-        # two-launch prefill and the decode at the workload's length, timed like the lines above
+        # single-kernel prefill and the decode at the workload's length, timed like the lines above
         scheds = {}
         for name in ("grouped", "seam", "fractional"):
-            jl.jl_bifocal_prefill_sched(q, k, v, out, lse, big_l, w, base, name, ws_pre)
+            jl.jl_bifocal_prefill_sched(q, k, v, out, lse, big_l, w, base, name)
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
             for e in ev:
                 e[0].record(stream)
-                jl.jl_bifocal_prefill_sched(q, k, v, out, lse, big_l, w, base, name, ws_pre)
+                jl.jl_bifocal_prefill_sched(q, k, v, out, lse, big_l, w, base, name)
                 e[1].record(stream)
             torch.cuda.synchronize()
             sp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))

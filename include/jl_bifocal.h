@@ -3,25 +3,27 @@
  *
  * The operation is the attention of Jet-Long's Dynamic Bifocal RoPE
  * (arXiv 2607.07740), as described by:
- *   - ResearchPod summary (researchpod.app), 2nd paragraph: a local window that
- *     keeps the original RoPE; a remote window whose positions are aliased by
- *     the smallest integer grouping g that keeps remote rotation angles inside
- *     the pretrained range; an inclusion-exclusion merge of three
- *     FlashAttention passes fused into one kernel.
- *   - ResearchPod transcript, exchange on the cache: the cache keeps the
- *     original, uncompressed positions and the remapping correction is applied
- *     at lookup time.
- *   - ResearchPod transcript, exchange on prefill: the merge combines the local
- *     view, the remapped distant view and a corrected version of the local view.
- *   - Abstract (engineersofai.com paper page): exact recovery of the base model
- *     at short inputs; inclusion-exclusion attention merge and an on-the-fly RoPE
- *     correction rotation.
+ *   - ResearchPod summary (researchpod.app), 2nd paragraph: nearby keys are scored
+ *     with the base RoPE; distant positions are folded onto a coarser grid whose
+ *     step g is the least integer that holds every folded position inside the
+ *     positions seen in training; three FlashAttention-style passes are combined
+ *     by inclusion-exclusion in one fused kernel.
+ *   - ResearchPod transcript, exchange on the cache: the cache holds every key at
+ *     the position it was written at, and the folding is applied when the key is
+ *     read.
+ *   - ResearchPod transcript, exchange on prefill: the merged result is built from
+ *     the near keys at base positions, all keys at folded positions, and the near
+ *     keys at folded positions (subtracted).
+ *   - Abstract (engineersofai.com paper page): at short inputs the base model is
+ *     recovered exactly; the merge and the rotation that moves cached vectors to
+ *     their folded positions are computed inside the attention kernel.
  *   - seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap":
- *     the long-range factor is computed from the current sequence length s.
+ *     the long-range factor is derived from the current sequence length s.
  *
  * Definitions used by every entry point (head size D = 128):
  *   s      = n_kv, the number of keys in context (cache index == position).
- *   p_i    = n_kv - n_q + i, position of query row i (the newest n_q tokens).
+ *   p_i    = n_kv - n_q + i, position of query row i (the newest n_q tokens),
+ *            or q_pos[i] where an entry point takes explicit positions.
  *   theta_d= rope_base^(-2d/D), rotate-half pairs (d, d + D/2).
  *   g      = jl_group_factor(s, L) = smallest integer >= 1 with
  *            floor((s-1)/g) <= L-1  (== max(1, ceil(s/L))).
@@ -75,25 +77,37 @@ const char* jl_last_error(void);
 
 /* g(s): smallest integer g >= 1 with floor((s-1)/g) <= L-1, i.e. every aliased
  * position floor(p/g), p < s, falls inside the pretrained positions 0..L-1
- * (ResearchPod summary, 2nd paragraph: "smallest integer grouping").
+ * (ResearchPod summary, 2nd paragraph: the factor is the least integer that
+ * keeps the folded positions inside the trained range).
  * Pure integer host function.  Returns 0 if seq_len < 1 or pretrained_window < 1. */
 int64_t jl_group_factor(int64_t seq_len, int64_t pretrained_window);
 
-/* Bifocal prefill (or a chunk of queries against a longer context).
- *   q    : bf16 [B, n_q, Hq, D], rotated at positions p_i (as the model produced them)
- *   k, v : bf16 [B, n_kv, Hkv, D], k rotated at its original positions 0..n_kv-1
- *   out  : bf16 [B, n_q, Hq, D] (written)
- *   lse  : fp32 [B, Hq, n_q] natural-log normaliser of the merged softmax, or NULL
+/* Bifocal prefill (or a chunk of queries against a longer context), in one
+ * kernel launch.
+ *   q     : bf16 [B, n_q, Hq, D], rotated at positions p_i (as the model produced them)
+ *   k, v  : bf16 [B, n_kv, Hkv, D], k rotated at its original positions 0..n_kv-1
+ *   out   : bf16 [B, n_q, Hq, D] (written)
+ *   lse   : fp32 [B, Hq, n_q] natural-log normaliser of the merged softmax, or NULL
+ *   q_pos : NULL: row i sits at p_i = n_kv - n_q + i (the newest n_q tokens).
+ *           Otherwise a device int32 [n_q], 4-byte aligned, nondecreasing, each
+ *           in [0, n_kv), shared by every sequence of the batch: row i sits at
+ *           q_pos[i] (ResearchPod transcript, cache exchange: keys keep their
+ *           original positions, so any query position can be scored against
+ *           them).  Not read on the host: entries outside the contract give an
+ *           unspecified result, never an access out of range (positions are
+ *           clamped into [0, n_kv)).
  * g = jl_group_factor(n_kv, L).  When g == 1 every remote rotation is the
  * original one and the call runs jl_plain_prefill (bitwise identical results:
- * the base model, Abstract "recovering the base model exactly").  Otherwise the
- * fused kernel applies the correction rotation c(p) to q and k on the fly and
- * evaluates the three-pass merge above.  Requires 1 <= W <= L. */
+ * the base model, Abstract: exact recovery at short inputs).  Otherwise the
+ * kernel rotates q and each staged key tile by the correction c(p) on the fly
+ * (the corrected keys never leave LDS) and evaluates the three-pass merge above.
+ * Requires 1 <= W <= L.  Errors: as listed above, plus JL_ERR_INVALID_ARG for a
+ * misaligned q_pos. */
 jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
-                             int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
-                             int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
-                             int64_t local_window, double rope_base, float softmax_scale,
-                             void* stream);
+                             const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                             int64_t pretrained_window, int64_t local_window, double rope_base,
+                             float softmax_scale, void* stream);
 
 /* Bytes of device workspace jl_bifocal_prefill_ws needs: one corrected copy of
  * the keys, bf16 [B, n_kv, Hkv, D].  0 for invalid sizes. */
@@ -104,10 +118,10 @@ size_t jl_bifocal_prefill_workspace_size(int32_t batch, int32_t n_kv, int32_t n_
  * k^g_j = rot(k_j, c(j) theta) for every cached key to `workspace` (bf16,
  * layout of k), then the attention kernel stages those corrected keys like
  * plain keys instead of rotating every key tile once per query block.  The
- * cache itself is not modified.  The pages fuse the correction into the one
- * attention kernel (Jet-Long summary page: a single fused kernel, no extra
- * pass); on this GPU the extra pass is cheaper than repeating the rotation per
- * query block, so this entry point trades workspace for speed.
+ * cache itself is not modified.  This departs from the method as described,
+ * which corrects the keys inside the one attention kernel (jl_bifocal_prefill);
+ * it keeps a corrected copy of the keys for the duration of the call and
+ * trades that workspace for speed.  Always uses the newest-rows positions.
  *   workspace       : device memory, 16-byte aligned, owned by the caller; it
  *                     may be NULL when g(n_kv) == 1 (the plain path needs none),
  *                     otherwise NULL or misaligned is JL_ERR_INVALID_ARG
@@ -122,10 +136,11 @@ jl_status jl_bifocal_prefill_ws(const void* q, const void* k, const void* v, voi
 
 /* Plain causal RoPE attention built with the same kernel skeleton (the base
  * model; denominator of the "overhead vs plain" and "vs plain causal"
- * comparisons).  Same layouts as jl_bifocal_prefill. */
+ * comparisons).  Same layouts and q_pos contract as jl_bifocal_prefill. */
 jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
-                           int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
-                           int32_t n_kv_heads, int32_t head_dim, float softmax_scale, void* stream);
+                           const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           float softmax_scale, void* stream);
 
 /* Sliding-window attention: query row i attends to the keys j with
  * 0 <= p_i - j <= W-1 on the cached vectors (base RoPE), one softmax per row.
@@ -142,8 +157,9 @@ jl_status jl_sliding_prefill(const void* q, const void* k, const void* v, void* 
                              float softmax_scale, void* stream);
 
 /* Per-pass results of the three FlashAttention-style passes of the merge
- * (ResearchPod transcript, prefill exchange: local view A, remapped distant
- * view B, corrected local view C), each normalised on its own key set:
+ * (ResearchPod transcript, prefill exchange: A, the near keys at base positions;
+ * B, all keys at folded positions; C, the near keys at folded positions), each
+ * normalised on its own key set:
  *   out_abc : fp32 [3, B, n_q, Hq, D]   (pass A, then B, then C)
  *   lse_abc : fp32 [3, B, Hq, n_q]      natural log; -inf for an empty key set
  * For checking and debugging; slower than jl_bifocal_prefill.  Runs the three
@@ -296,19 +312,21 @@ jl_status jl_bifocal_decode_sched(const void* q, const void* k_cache, const void
  *   cu_seqlens_q  : device int32 [B+1], 4-byte aligned, non-decreasing from 0 to total_q
  *   seq_lens      : device int32 [B], 4-byte aligned, n_b <= s_b <= max_seq_len
  *   max_q         : host int, >= every n_b (sizes the grid), <= max_seq_len
- *   workspace     : >= jl_bifocal_prefill_workspace_size(B, max_seq_len, Hkv, D) bytes
- *                   (the corrected keys of every sequence; contents ignored on entry)
+ *   workspace     : NULL with workspace_bytes == 0: the keys are corrected inside the
+ *                   attention kernel (one launch, the form of jl_bifocal_prefill).
+ *                   Otherwise >= jl_bifocal_prefill_workspace_size(B, max_seq_len, Hkv, D)
+ *                   bytes for the corrected keys of every sequence, written by a first
+ *                   pass (the two-launch form; contents ignored on entry)
  * The device arrays are not read on the host: values outside the contract give an
  * unspecified result but no access outside q, out, lse or the caches.  A sequence
  * with n_b = 0 writes nothing.  Each sequence gets what jl_bifocal_prefill_sched
- * (two-launch form) returns for it alone, with n_q = n_b and n_kv = s_b.  With
- * every n_b and s_b equal it is that call on the padded batch, with the same
- * corrected keys and the same sweep; the compiler may fuse the fp32 products of
- * the query rotation differently in the two kernels, so a rare output differs by
- * bf16 rounding (jl_plain_prefill_varlen is bitwise jl_plain_prefill).  The
- * bifocal kernel runs for every sequence, so one with g = 1 is the base model up
- * to rounding order.  Errors as jl_bifocal_prefill_sched, plus JL_ERR_INVALID_ARG
- * for NULL or misaligned length arrays, total_q < 1 or max_q > max_seq_len. */
+ * (in the same form) returns for it alone, with n_q = n_b and n_kv = s_b.  With
+ * every n_b and s_b equal it is bitwise that call on the padded batch (same
+ * corrected keys, same sweep, same rounding; jl_plain_prefill_varlen is bitwise
+ * jl_plain_prefill).  The bifocal kernel runs for every sequence, so one with
+ * g = 1 is the base model up to rounding order.  Errors as
+ * jl_bifocal_prefill_sched, plus JL_ERR_INVALID_ARG for NULL or misaligned length
+ * arrays, total_q < 1 or max_q > max_seq_len. */
 jl_status jl_bifocal_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
                                     void* out, float* lse, const int32_t* cu_seqlens_q,
                                     const int32_t* seq_lens, int32_t batch, int32_t total_q,
@@ -380,11 +398,12 @@ jl_status jl_plain_decode_paged(const void* q, const void* k_pages, const void* 
  *           shared by every sequence of the batch; not read on the host: values
  *           outside the contract give an unspecified result, never an access out
  *           of range (positions are clamped into [0, n_kv))
- * Everything else as jl_bifocal_prefill_sched in its two-launch form (the
- * workspace is needed when g > 1) and jl_plain_prefill.  Row i gets what the
- * whole prefill of n_kv queries gives at position q_pos[i], up to rounding
- * order.  Errors as those calls, plus JL_ERR_INVALID_ARG for a NULL or
- * misaligned q_pos. */
+ * Everything else as jl_bifocal_prefill_sched: with a workspace the corrected
+ * keys are written there first (two launches), with workspace == NULL and
+ * workspace_bytes == 0 they are corrected inside the attention kernel (one
+ * launch, as jl_bifocal_prefill with q_pos).  Row i gets what the whole prefill
+ * of n_kv queries gives at position q_pos[i], up to rounding order.  Errors as
+ * those calls, plus JL_ERR_INVALID_ARG for a NULL or misaligned q_pos. */
 jl_status jl_bifocal_prefill_positions(const void* q, const void* k, const void* v, void* out,
                                        float* lse, const int32_t* q_pos, int32_t batch, int32_t n_q,
                                        int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
@@ -410,7 +429,7 @@ jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v
  *      to rows p of the caches (the cache keeps original positions: ResearchPod
  *      transcript, cache exchange);
  *   3. attention of the n_new queries over the n_kv cached keys: JL_LAYER_BIFOCAL
- *      is jl_bifocal_prefill_sched in its two-launch form (n_new > 1) or
+ *      is jl_bifocal_prefill_sched in its single-kernel form (n_new > 1) or
  *      jl_bifocal_decode_sched (n_new == 1) under `schedule`; JL_LAYER_PLAIN is
  *      plain causal attention (jl_plain_prefill / jl_plain_decode); scale 1/sqrt(128);
  *   4. out = attn w_o^T (rocBLAS), no bias.
@@ -426,8 +445,11 @@ jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v
  *   workspace     : >= jl_qwen3_layer_workspace_size(...) bytes of device memory,
  *                   16-byte aligned, contents ignored on entry
  * All pointers are device pointers, 16-byte aligned, owned by the caller; the
- * layer runs in stream order on `stream` and allocates nothing (rocBLAS keeps one
- * handle per calling thread and device, created on first use).  Windows and
+ * layer runs in stream order on `stream`.  Device memory: the library allocates
+ * none.  Projections of more than 8 rows run on rocBLAS through one handle per
+ * calling thread and device (created on first use, destroyed when the thread
+ * exits), whose GEMM scratch is a 32 MiB part of `workspace`; creating a handle
+ * is rocBLAS's own work and may allocate inside rocBLAS.  Windows and
  * schedule are checked as in jl_bifocal_prefill_sched when attention ==
  * JL_LAYER_BIFOCAL and ignored otherwise (rope_base is always checked).
  * Errors: JL_ERR_INVALID_ARG for bad pointers, sizes (n_new > n_kv, hidden < 1),

@@ -8,17 +8,18 @@ or helper with the HIP library, and it imports nothing from it.
 Every function follows a passage of the pages about Jet-Long (arXiv 2607.07740),
 cited by page and section:
 
-* ResearchPod summary (researchpod.app), 2nd paragraph: local window on the
-  original RoPE; remote keys aliased by the *smallest integer grouping* that keeps
-  remote rotation angles inside the pretrained distribution; an
-  inclusion-exclusion merge of three FlashAttention passes.
-* ResearchPod transcript, the exchange on the cache: the cache keeps the original,
-  uncompressed positions and the remapping correction is applied at lookup.
-* ResearchPod transcript, the exchange on prefill: the merge combines a local
-  view, a remapped distant view and a corrected version of the local view.
-* Abstract (engineersofai.com paper page): recovers the base model exactly at
-  short inputs; inclusion-exclusion attention merge plus an on-the-fly RoPE
-  correction rotation.
+* ResearchPod summary (researchpod.app), 2nd paragraph: nearby keys keep the
+  base RoPE; distant positions are folded onto a coarser grid whose step is the
+  least integer that holds every folded position inside the trained range; three
+  FlashAttention-style passes are combined by inclusion-exclusion.
+* ResearchPod transcript, the exchange on the cache: every key stays in the cache
+  at the position it was written at; the folding is applied when it is read.
+* ResearchPod transcript, the exchange on prefill: the result is built from the
+  near keys at base positions, all keys at folded positions, and the near keys
+  at folded positions.
+* Abstract (engineersofai.com paper page): the base model is recovered exactly at
+  short inputs; the merge and the rotation to folded positions run inside the
+  attention kernel.
 * seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap": the
   long-range factor is computed from the current sequence length s; the merge
   combines the branches without double-counting.

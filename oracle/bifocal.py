@@ -170,7 +170,7 @@ def long_range_schedule(seq_len: int, pretrained_window: int, local_window: int,
     long-range branch.  The local branch always keeps the original positions.
 
     * ``grouped`` (the reading used everywhere else): a(p) = p // g on both sides
-      (ResearchPod summary, 2nd paragraph: smallest integer grouping).
+      (ResearchPod summary, 2nd paragraph: the least integer factor).
     * ``seam``: keys at j // g, queries at p // g + W - W // g.  The shift makes a
       remote distance continue the local window's distances at the seam; g grows
       to keep the shifted distances inside L.
@@ -364,20 +364,20 @@ def bifocal_three_pass(q, k, v, pretrained_window, local_window, rope_base,
                        softmax_scale=None, rows=None, row_block=128, schedule="grouped", positions=None):
     """Bifocal attention as three FlashAttention-style passes and their merge.
 
-    ResearchPod summary, 2nd paragraph (three passes, smallest integer grouping);
-    ResearchPod transcript, prefill exchange (local view, remapped distant view,
-    corrected local view); ResearchPod transcript, cache exchange (keys kept at
-    original positions, correction applied at lookup).
+    ResearchPod summary, 2nd paragraph (three passes, the least integer factor);
+    ResearchPod transcript, prefill exchange (near keys at base positions, all keys
+    folded, near keys folded); ResearchPod transcript, cache exchange (keys kept at
+    original positions, correction applied when read).
 
     Inputs are the cached vectors, already rotated at their original positions
     (``q`` at ``p_i``, ``k`` at ``j``).  Per query row i (position p_i):
 
     * Loc_i = {j : 0 <= p_i - j <= W - 1}  (W keys including the query itself),
       All_i = {j : j <= p_i}.
-    * Pass A ("local view"):       keys Loc_i, scores tau * q_i . k_j.
-    * Pass B ("remapped distant"): keys All_i, scores tau * q^g_i . k^g_j with
+    * Pass A (near keys, base):    keys Loc_i, scores tau * q_i . k_j.
+    * Pass B (all keys, folded):   keys All_i, scores tau * q^g_i . k^g_j with
       q^g_i = rot(q_i, c(p_i) theta), k^g_j = rot(k_j, c(j) theta).
-    * Pass C ("corrected local"):  keys Loc_i, the grouped scores of pass B.
+    * Pass C (near keys, folded):  keys Loc_i, the grouped scores of pass B.
     * Merge: ``merge_passes``.
 
     Readings: absolute-position aliasing a(p) = p // g on both sides; no seam

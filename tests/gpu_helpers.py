@@ -1,20 +1,39 @@
 """Helpers for the GPU parity tests: device upload of the seeded bf16 inputs and
-the parity bar (max-abs <= 1e-2 and mean-abs <= 1e-3 against the fp64 oracle,
-bf16 inputs with fp32 accumulation).
+the parity bar against the fp64 oracle (bf16 inputs with fp32 accumulation):
+outputs max-abs <= 1e-2 and mean-abs <= 1e-3.
 
-The same bar applies to the natural-log normaliser (lse).  Its error is set by
-the scores: the corrected vectors q^g and k^g are rounded to bf16 before the
-MFMA (relative error up to 2^-8 per element, bf16's unit roundoff), which moves a grouped score
-tau * q^g . k^g by ~2e-3 RMS for N(0,1) inputs at D = 128, and the lse of a short
-row inherits that directly."""
+The natural-log normaliser (lse) has a bar of its own (lse_tol).  Where every
+score is taken on the vectors as given (plain attention, g = 1, sliding windows)
+the kernels sum fp32 probabilities, so the lse carries fp32 rounding only and
+the bar is 1e-3.  With g > 1 two further errors enter:
+- grouped scores use q^g and k^g rounded to bf16 before the MFMA: each element
+  carries a relative error of RMS ~1.6e-3 (round to nearest with 8 significant
+  bits), which moves a score tau * q^g . k^g by ~1.6e-3 * sqrt(2 D) / sqrt(D) =
+  2.3e-3 RMS for N(0, 1) inputs at D = 128;
+- the single-kernel form sums the bf16-rounded probabilities (one instruction
+  per pair in the loop that kernel is bound by): the normaliser's relative error
+  is a weighted mean of roundings of at most 2^-8, RMS ~2.2e-3 at most.
+The lse moves by the softmax-weighted mean of these errors, RMS up to
+sqrt(2.3^2 + 2.2^2) e-3 * sqrt(sum_j p_j^2): 3.2e-3 only where one key holds all
+the weight, far less once the weight is spread over the W + 1 or more keys of a
+row with remote keys.  The bar is 4e-3; the largest lse error measured over
+these tests is 1.6e-3.  The mean-abs bar stays 1e-3 for both.
+"""
 
 import numpy as np
 import torch
 
 MAX_ABS_TOL = 1e-2
 MEAN_ABS_TOL = 1e-3
-LSE_TOL = MAX_ABS_TOL
+LSE_TOL_PLAIN = 1e-3    # scores on the vectors as given
+LSE_TOL_GROUPED = 4e-3  # grouped scores on bf16-rounded corrected vectors
+LSE_TOL = LSE_TOL_GROUPED
 LSE_MEAN_TOL = MEAN_ABS_TOL
+
+
+def lse_tol(g: int) -> float:
+    """Max-abs bar of the lse for a call whose group factor is g (1: the base model)."""
+    return LSE_TOL_PLAIN if g == 1 else LSE_TOL_GROUPED
 
 
 def to_device(bits: np.ndarray) -> torch.Tensor:

@@ -65,16 +65,16 @@ def test_group_factor_bit_exact_with_oracle(lib):
 
 
 def _prefill(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, batch=1, n_q=64, n_kv=64, hq=4, hkv=2, d=128,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, pos=None, batch=1, n_q=64, n_kv=64, hq=4, hkv=2, d=128,
              big_l=32, w=8, base=1e4, scale=0.0)
     a.update(kw)
-    return lib.jl_bifocal_prefill(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["n_q"], a["n_kv"],
-                                  a["hq"], a["hkv"], a["d"], a["big_l"], a["w"], a["base"], a["scale"], None)
+    return lib.jl_bifocal_prefill(a["q"], a["k"], a["v"], a["out"], a["lse"], a["pos"], a["batch"], a["n_q"],
+                                  a["n_kv"], a["hq"], a["hkv"], a["d"], a["big_l"], a["w"], a["base"], a["scale"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
-    (dict(q=FAKE + 2), INVALID), (dict(lse=FAKE + 4), INVALID),
+    (dict(q=FAKE + 2), INVALID), (dict(lse=FAKE + 4), INVALID), (dict(pos=FAKE + 2), INVALID),
     (dict(batch=0), INVALID), (dict(n_q=0), INVALID), (dict(n_kv=-3), INVALID), (dict(hq=0), INVALID),
     (dict(n_q=65), INVALID), (dict(hq=3, hkv=2), INVALID),
     (dict(big_l=0), INVALID), (dict(w=0), INVALID), (dict(w=33), INVALID),
@@ -94,7 +94,10 @@ def test_no_device_reports_device_error(lib):
         pytest.skip("a GPU is present")
     assert _prefill(lib) == DEVICE
     assert b"device" in lib.jl_last_error()
-    assert lib.jl_plain_prefill(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 8, 1, 1, 128, 0.0, None) == DEVICE
+    assert _prefill(lib, pos=FAKE) == DEVICE      # explicit positions: same single kernel
+    assert lib.jl_plain_prefill(FAKE, FAKE, FAKE, FAKE, None, None, 1, 8, 8, 1, 1, 128, 0.0, None) == DEVICE
+    assert lib.jl_plain_prefill(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 8, 8, 1, 1, 128, 0.0, None) == DEVICE
+    assert lib.jl_plain_prefill(FAKE, FAKE, FAKE, FAKE, None, FAKE + 1, 1, 8, 8, 1, 1, 128, 0.0, None) == INVALID
     assert lib.jl_bifocal_prefill_passes(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 1, 1, 128, 4, 2, 1e4, 0.0,
                                          None) == DEVICE
     ws = lib.jl_bifocal_decode_workspace_size(1, 100, 4, 2, 128)
@@ -280,13 +283,15 @@ def test_schedule_entry_points_validation(lib):
 
 def test_layer_workspace_and_validation(lib):
     # projected q/k/v + rotated q + attention output (256-byte aligned regions), then the
-    # attention's workspace: corrected keys for a prefill, the decode partials for one token
+    # attention's workspace (none for a prefill, the decode partials for one token), then
+    # 32 MiB of scratch for the library GEMMs
     t, hq, hkv = 2 * 100, 8, 2
     up = lambda x: (x + 255) // 256 * 256
-    pre = up(t * (hq + 2 * hkv) * 256) + 2 * up(t * hq * 256) + up(2 * 300 * hkv * 256)
+    gemm = 32 << 20
+    pre = up(t * (hq + 2 * hkv) * 256) + 2 * up(t * hq * 256) + gemm
     assert lib.jl_qwen3_layer_workspace_size(2, 100, 300, hq, hkv, 128) == pre
     dec = up(2 * (hq + 2 * hkv) * 256) + 2 * up(2 * hq * 256) + up(lib.jl_bifocal_decode_workspace_size(2, 300, hq,
-                                                                                                          hkv, 128))
+                                                                                                          hkv, 128)) + gemm
     assert lib.jl_qwen3_layer_workspace_size(2, 1, 300, hq, hkv, 128) == dec
     assert lib.jl_qwen3_layer_workspace_size(2, 301, 300, hq, hkv, 128) == 0
     assert lib.jl_qwen3_layer_workspace_size(2, 100, 300, hq, hkv, 64) == 0
@@ -351,7 +356,9 @@ def test_prefill_varlen_validation(lib):
         if not _has_gpu():
             assert call() == DEVICE
     assert bif(wsb=need - 1) == WORKSPACE
-    assert bif(ws=None) == INVALID
+    assert bif(ws=None) == INVALID                   # a size without a workspace
+    if not _has_gpu():
+        assert bif(ws=None, wsb=0) == DEVICE         # no workspace: the single-kernel form
     assert bif(sched=1, w=64) == INVALID             # seam needs W < L
     assert bif(w=65) == INVALID
 
@@ -385,6 +392,8 @@ def test_prefill_positions_validation(lib):
     assert bif(sched=1, w=32) == INVALID
     if not _has_gpu():
         assert bif(L=128, ws=None, wsb=0) == DEVICE      # g = 1: no workspace needed
+        assert bif(ws=None, wsb=0) == DEVICE             # no workspace: the single-kernel form
+    assert bif(ws=None, wsb=need) == INVALID             # a size without a workspace
 
 
 def _header_signatures():

@@ -1,9 +1,11 @@
 """GPU parity at the full workload sizes, on sampled rows.
 
-Rows are independent, so the oracle computes a sample of rows exactly (first
-rows, rows around p = W, around L and next to multiples of g, the middle, the
-last rows, random rows) for a subset of heads, while the GPU runs the whole
-problem in the same launch configuration the bench times.
+Rows are independent, so the oracle computes a sample of rows exactly while the
+GPU runs the whole problem in the launch configuration the bench times.  The
+sample holds runs of 16 consecutive rows in five query blocks (the first rows,
+the rows around p = W where remote keys appear, around p = L, the middle and
+the last rows) plus rows next to multiples of g, over every KV head (so every
+workgroup-to-head mapping of the grid is checked), for both prefill forms.
 """
 
 import numpy as np
@@ -14,7 +16,7 @@ import oracle
 import zero_shot_rope_attention_amd as jl
 from zero_shot_rope_attention_amd.inputs import bf16_bits_to_f64, make_qkv
 
-from gpu_helpers import LSE_MEAN_TOL, LSE_TOL, assert_parity, sample_rows, to_device, to_f64
+from gpu_helpers import LSE_MEAN_TOL, assert_parity, lse_tol, sample_rows, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -27,28 +29,47 @@ FULL = {
 }
 
 
+def full_rows(s, big_l, w, g):
+    """Runs of 16 rows at the start, around W, around L, in the middle and at the
+    end, plus the seam and random rows of sample_rows: 80 rows or more."""
+    runs = [np.arange(a, a + 16) for a in (0, w - 8, big_l - 8, s // 2 - 8, s - 16)]
+    rows = np.concatenate(runs + [sample_rows(s, s, big_l, w, g, count=24)])
+    return np.unique(np.clip(rows, 0, s - 1))
+
+
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled_rows(name):
     wid, s, hq, hkv, big_l, w, base = FULL[name]
     g = oracle.group_factor(s, big_l)
-    print(f"full size {name}: s={s} Hq={hq} Hkv={hkv} g={g}", flush=True)
     qb, kb, vb = make_qkv(wid, 1, s, s, hq, hkv, 128)
     q, k, v = to_device(qb), to_device(kb), to_device(vb)
-    out = torch.empty_like(q)
-    lse = torch.empty((1, hq, s), dtype=torch.float32, device="cuda:0")
-    jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
-    torch.cuda.synchronize()
-    rows = sample_rows(s, s, big_l, w, g, count=20)
+    rows = full_rows(s, big_l, w, g)
     grp = hq // hkv
     kf, vf = bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
-    for kvh in (0, hkv - 1):
+    refs = []
+    for kvh in range(hkv):
         heads = slice(kvh * grp, (kvh + 1) * grp)
-        ref = oracle.bifocal_three_pass(bf16_bits_to_f64(qb[:, :, heads]), kf[:, :, kvh:kvh + 1],
-                                        vf[:, :, kvh:kvh + 1], big_l, w, base, rows=rows)
-        got = to_f64(out[:, rows, heads])
-        assert_parity(got, ref["out"], f"{name} kv head {kvh}")
-        got_lse = lse[:, heads][:, :, rows].cpu().numpy().astype(np.float64)
-        assert_parity(got_lse, ref["lse"], "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+        refs.append(oracle.bifocal_three_pass(bf16_bits_to_f64(qb[:, :, heads]), kf[:, :, kvh:kvh + 1],
+                                              vf[:, :, kvh:kvh + 1], big_l, w, base, rows=rows))
+        assert refs[-1]["g"] == g == jl.jl_group_factor(s, big_l)
+    ws = torch.empty(jl.jl_bifocal_prefill_workspace_size(1, s, hkv), dtype=torch.uint8, device="cuda:0")
+    for form in ("fused", "two_launch"):
+        print(f"full size {name}: s={s} Hq={hq} Hkv={hkv} g={g} form={form}, {len(rows)} rows x {hkv} KV heads",
+              flush=True)
+        out = torch.empty_like(q)
+        lse = torch.empty((1, hq, s), dtype=torch.float32, device="cuda:0")
+        if form == "fused":
+            jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
+        else:
+            jl.jl_bifocal_prefill_ws(q, k, v, out, lse, big_l, w, base, ws)
+        torch.cuda.synchronize()
+        got = to_f64(out[:, rows])
+        got_lse = lse[:, :, rows].cpu().numpy().astype(np.float64)
+        for kvh in range(hkv):
+            heads = slice(kvh * grp, (kvh + 1) * grp)
+            assert_parity(got[:, :, heads], refs[kvh]["out"], f"{name} {form} kv head {kvh}")
+            assert_parity(got_lse[:, heads], refs[kvh]["lse"], "lse", max_tol=lse_tol(g), mean_tol=LSE_MEAN_TOL)
+        del out, lse
 
 
 @pytest.mark.parametrize("s", [4096, 16384, 32768])

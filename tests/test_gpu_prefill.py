@@ -15,7 +15,7 @@ import oracle
 import zero_shot_rope_attention_amd as jl
 from zero_shot_rope_attention_amd.inputs import bf16_bits_to_f64, make_qkv
 
-from gpu_helpers import LSE_MEAN_TOL, LSE_TOL, assert_parity, to_device, to_f64
+from gpu_helpers import LSE_MEAN_TOL, LSE_TOL_PLAIN, assert_parity, lse_tol, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,7 @@ def test_bifocal_prefill_parity(case):
     ref = oracle.bifocal_three_pass(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb), big_l, w, base)
     assert ref["g"] == jl.jl_group_factor(n_kv, big_l)
     assert_parity(out, ref["out"])
-    assert_parity(lse, ref["lse"], "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+    assert_parity(lse, ref["lse"], "lse", max_tol=lse_tol(ref["g"]), mean_tol=LSE_MEAN_TOL)
 
 
 def test_bifocal_prefill_peaked_scores():
@@ -83,21 +83,21 @@ def test_short_input_is_plain_attention_bitwise(case):
     assert np.array_equal(out, out_p) and np.array_equal(lse, lse_p)
     ref, ref_lse = oracle.plain_causal_attention(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb))
     assert_parity(out, ref)
-    assert_parity(lse, ref_lse, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+    assert_parity(lse, ref_lse, "lse", max_tol=LSE_TOL_PLAIN, mean_tol=LSE_MEAN_TOL)
 
 
 def test_plain_prefill_parity_gqa_ragged():
     (qb, kb, vb), _, out, lse = _run(122, 1, 333, 1000, 8, 2, 1, 1, 1e4, plain=True)
     ref, ref_lse = oracle.plain_causal_attention(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb))
     assert_parity(out, ref)
-    assert_parity(lse, ref_lse, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+    assert_parity(lse, ref_lse, "lse", max_tol=LSE_TOL_PLAIN, mean_tol=LSE_MEAN_TOL)
 
 
 @pytest.mark.parametrize("case", [(130, 1, 2048, 2048, 1, 1, 512, 128, 1e4), (131, 1, 300, 300, 4, 2, 64, 40, 1e4),
                                   (132, 1, 200, 200, 2, 1, 256, 32, 1e4)])
 def test_three_passes_match_oracle_passes(case):
-    # The per-pass results (local view A, remapped distant view B, corrected
-    # local view C), each against the oracle's pass, plus their merge.
+    # The per-pass results (A: near keys at base positions, B: all keys folded,
+    # C: near keys folded), each against the oracle's pass, plus their merge.
     wid, b, n_q, n_kv, hq, hkv, big_l, w, base = case
     qb, kb, vb = make_qkv(wid, b, n_q, n_kv, hq, hkv, 128)
     q, k, v = to_device(qb), to_device(kb), to_device(vb)
@@ -110,7 +110,9 @@ def test_three_passes_match_oracle_passes(case):
     ls = lse_abc.cpu().numpy().astype(np.float64)
     for i, name in enumerate("ABC"):
         assert_parity(o[i], ref["passes"][name][0], f"pass {name}")
-        assert_parity(ls[i], ref["passes"][name][1], f"lse {name}", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+        # pass A scores the vectors as given; B and C score the rounded corrected ones
+        tol = LSE_TOL_PLAIN if name == "A" else lse_tol(ref["g"])
+        assert_parity(ls[i], ref["passes"][name][1], f"lse {name}", max_tol=tol, mean_tol=LSE_MEAN_TOL)
     merged, merged_lse = oracle.merge_passes(o[0], ls[0], o[1], ls[1], o[2], ls[2])
     assert_parity(merged, ref["out"], "merge of GPU passes")
 
@@ -141,7 +143,13 @@ def test_rows_without_remote_keys_match_plain():
     wid, b, n_q, n_kv, hq, hkv, big_l, w, base = 141, 1, 900, 900, 2, 1, 200, 150, 1e4
     _, _, out, _ = _run(wid, b, n_q, n_kv, hq, hkv, big_l, w, base)
     _, _, out_p, _ = _run(wid, b, n_q, n_kv, hq, hkv, big_l, w, base, plain=True)
-    assert_parity(out[:, :w], out_p[:, :w], "rows p < W vs plain", max_tol=2e-3, mean_tol=1e-4)
+    # the same keys and scores; the two kernels normalise with different row sums (the
+    # single-kernel bifocal form adds the bf16-rounded probabilities, the plain kernel the
+    # fp32 ones), which can move an output by one bf16 rounding step
+    a, b_ = out[:, :w], out_p[:, :w]
+    d = np.abs(a - b_)
+    print(f"rows p < W vs plain: max-abs {d.max():.3e}, mean-abs {d.mean():.3e}", flush=True)
+    assert np.all(d <= 2.0 ** -7 * np.abs(b_) + 2e-3) and d.mean() <= 1e-4
 
 
 def test_chunked_prefill_as_the_cache_grows():
@@ -170,6 +178,6 @@ def test_chunked_prefill_as_the_cache_grows():
                 jl.jl_bifocal_prefill_ws(qc, kc, vc, out, lse, big_l, w, base, ws)
             torch.cuda.synchronize()
             assert_parity(to_f64(out), ref["out"], f"chunk [{lo}, {hi}) {form}")
-            assert_parity(lse.cpu().numpy().astype(np.float64), ref["lse"], "lse", max_tol=LSE_TOL,
+            assert_parity(lse.cpu().numpy().astype(np.float64), ref["lse"], "lse", max_tol=lse_tol(ref["g"]),
                           mean_tol=LSE_MEAN_TOL)
     assert seen == [1, 2, 2, 3, 3]

@@ -16,7 +16,7 @@ import oracle
 import zero_shot_rope_attention_amd as jl
 from zero_shot_rope_attention_amd.inputs import bf16_bits_to_f64, normal_bf16
 
-from gpu_helpers import LSE_MEAN_TOL, LSE_TOL, assert_parity, to_device, to_f64
+from gpu_helpers import LSE_MEAN_TOL, LSE_TOL, LSE_TOL_PLAIN, assert_parity, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def _inputs(seed, spec, hq, hkv, n_max=None):
     return qb, kb, vb, cu
 
 
-def _run(qb, kb, vb, cu, spec, big_l=None, w=None, base=None, schedule="grouped", plain=False):
+def _run(qb, kb, vb, cu, spec, big_l=None, w=None, base=None, schedule="grouped", plain=False, form="fused"):
     total_q, hq, _ = qb.shape
     b, n_max, hkv = kb.shape[0], kb.shape[1], kb.shape[2]
     q, kc, vc = to_device(qb), to_device(kb), to_device(vb)
@@ -45,12 +45,14 @@ def _run(qb, kb, vb, cu, spec, big_l=None, w=None, base=None, schedule="grouped"
     cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
     sl = torch.tensor([s for _, s in spec], dtype=torch.int32, device="cuda:0")
     max_q = max(n for n, _ in spec)
-    print(f"prefill varlen spec={spec} Hq={hq} Hkv={hkv} L={big_l} W={w} schedule={schedule} plain={plain}",
-          flush=True)
+    print(f"prefill varlen spec={spec} Hq={hq} Hkv={hkv} L={big_l} W={w} schedule={schedule} plain={plain} "
+          f"form={form}", flush=True)
     if plain:
         jl.jl_plain_prefill_varlen(q, kc, vc, out, lse, cu_d, sl, max_q)
     else:
-        ws = torch.empty(jl.jl_bifocal_prefill_workspace_size(b, n_max, hkv), dtype=torch.uint8, device="cuda:0")
+        # the single kernel takes no workspace; the two-launch form writes the corrected keys there first
+        ws = None if form == "fused" else torch.empty(jl.jl_bifocal_prefill_workspace_size(b, n_max, hkv),
+                                                       dtype=torch.uint8, device="cuda:0")
         jl.jl_bifocal_prefill_varlen(q, kc, vc, out, lse, cu_d, sl, max_q, big_l, w, base, ws, schedule=schedule)
     torch.cuda.synchronize()
     return to_f64(out), lse.cpu().numpy().astype(np.float64), (q, kc, vc)
@@ -71,21 +73,26 @@ CASES = [
 ]
 
 
+FORMS = ["fused", "two_launch"]
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}" for c in CASES])
-def test_prefill_varlen_parity(case):
+def test_prefill_varlen_parity(case, form):
     seed, spec, hq, hkv, big_l, w, base = case
     qb, kb, vb, cu = _inputs(seed, spec, hq, hkv)
-    out, lse, _ = _run(qb, kb, vb, cu, spec, big_l, w, base)
+    out, lse, _ = _run(qb, kb, vb, cu, spec, big_l, w, base, form=form)
     ro, rl = _oracle(qb, kb, vb, cu, spec, big_l, w, base)
     assert_parity(out, ro)
     assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("schedule", ["seam", "fractional"])
-def test_prefill_varlen_schedules(schedule):
+def test_prefill_varlen_schedules(schedule, form):
     spec = [(300, 300), (77, 900), (1, 333), (250, 1300)]
     qb, kb, vb, cu = _inputs(610, spec, 8, 2)
-    out, lse, _ = _run(qb, kb, vb, cu, spec, 256, 64, 1e4, schedule=schedule)
+    out, lse, _ = _run(qb, kb, vb, cu, spec, 256, 64, 1e4, schedule=schedule, form=form)
     ro, rl = _oracle(qb, kb, vb, cu, spec, 256, 64, 1e4, schedule=schedule)
     assert_parity(out, ro)
     assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
@@ -97,24 +104,25 @@ def test_plain_prefill_varlen_parity():
     out, lse, _ = _run(qb, kb, vb, cu, spec, plain=True)
     ro, rl = _oracle(qb, kb, vb, cu, spec, None, None, None, plain=True)
     assert_parity(out, ro)
-    assert_parity(lse, rl, "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+    assert_parity(lse, rl, "lse", max_tol=LSE_TOL_PLAIN, mean_tol=LSE_MEAN_TOL)
 
 
-@pytest.mark.parametrize("plain", [False, True])
-def test_equal_lengths_match_the_uniform_call(plain):
-    # two sequences of 333 new rows over 1000 keys against the padded-batch call.
-    # Plain: bit for bit.  Bifocal: the corrected keys are bit for bit the same and
-    # so is the kernel's sweep, but the compiler may fuse the fp32 products of the
-    # query rotation differently in the two kernel variants, which moves a rare
-    # query element by one bf16 ulp: a few outputs then differ at bf16 rounding.
+@pytest.mark.parametrize("form", ["plain"] + FORMS)
+def test_equal_lengths_match_the_uniform_call(form):
+    # two sequences of 333 new rows over 1000 keys against the padded-batch call of
+    # the same form: the same corrected keys, the same sweep and the same rounding
+    # (every rotation is written with explicit fused multiply-adds), so bit for bit
     spec = [(333, 1000), (333, 1000)]
+    plain = form == "plain"
     qb, kb, vb, cu = _inputs(630, spec, 8, 2)
-    out, lse, (q, kc, vc) = _run(qb, kb, vb, cu, spec, 256, 64, 1e4, plain=plain)
+    out, lse, (q, kc, vc) = _run(qb, kb, vb, cu, spec, 256, 64, 1e4, plain=plain, form=form)
     q_u = q.view(2, 333, 8, 128)
     out_u = torch.empty_like(q_u)
     lse_u = torch.empty((2, 8, 333), dtype=torch.float32, device="cuda:0")
     if plain:
         jl.jl_plain_prefill(q_u, kc, vc, out_u, lse_u)
+    elif form == "fused":
+        jl.jl_bifocal_prefill(q_u, kc, vc, out_u, lse_u, 256, 64, 1e4)
     else:
         ws = torch.empty(jl.jl_bifocal_prefill_workspace_size(2, 1000, 2), dtype=torch.uint8, device="cuda:0")
         jl.jl_bifocal_prefill_ws(q_u, kc, vc, out_u, lse_u, 256, 64, 1e4, ws)
@@ -124,21 +132,17 @@ def test_equal_lengths_match_the_uniform_call(plain):
     n_diff = np.count_nonzero(ou != out)
     print(f"varlen vs uniform: out differs in {n_diff} of {out.size}, max {np.abs(ou - out).max():.3e}; "
           f"lse differs in {np.count_nonzero(lu != lse)}, max {np.abs(lu - lse).max():.3e}", flush=True)
-    if plain:
-        assert n_diff == 0 and np.array_equal(lu, lse)
-    else:
-        assert n_diff <= out.size // 1000
-        assert np.all(np.abs(ou - out) <= 2.0 ** -7 * np.abs(ou) + 1e-3)
-        assert np.abs(lu - lse).max() <= 1e-4
+    assert n_diff == 0 and np.array_equal(lu, lse)
 
 
-def test_prefill_varlen_full_length_sampled():
+@pytest.mark.parametrize("form", FORMS)
+def test_prefill_varlen_full_length_sampled(form):
     # the Qwen3-8B decode-head shape: sequences of 16K and 40K keys with chunks of new rows;
     # sampled rows of every sequence against the oracle
     spec = [(4096, 16384), (1000, 40000), (2048, 2048)]
     hq, hkv, big_l, w, base = 32, 8, 8192, 1024, 1e6
     qb, kb, vb, cu = _inputs(640, spec, hq, hkv)
-    out, lse, _ = _run(qb, kb, vb, cu, spec, big_l, w, base)
+    out, lse, _ = _run(qb, kb, vb, cu, spec, big_l, w, base, form=form)
     kf, vf = bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
     for bi, (n, s) in enumerate(spec):
         rows = np.unique(np.clip(np.array([0, 1, n // 2, n - w - 1, n - w, n - 2, n - 1]), 0, n - 1))

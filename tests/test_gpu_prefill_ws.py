@@ -2,8 +2,9 @@
 a caller workspace, then staged like plain keys) against the fp64 oracle.
 
 Same cases and bar as the fused path (max-abs <= 1e-2, mean-abs <= 1e-3), plus
-the full 128K / 64K workloads on sampled rows, workspace reuse across calls of
-different sizes, and the g = 1 short-circuit (no workspace needed)."""
+workspace reuse across calls of different sizes and the g = 1 short-circuit (no
+workspace needed).  The full workload sizes are checked for both forms in
+test_gpu_full_sizes."""
 
 import numpy as np
 import pytest
@@ -13,8 +14,7 @@ import oracle
 import zero_shot_rope_attention_amd as jl
 from zero_shot_rope_attention_amd.inputs import bf16_bits_to_f64, make_qkv
 
-from gpu_helpers import LSE_MEAN_TOL, LSE_TOL, assert_parity, sample_rows, to_device, to_f64
-from test_gpu_full_sizes import FULL
+from gpu_helpers import LSE_MEAN_TOL, assert_parity, lse_tol, to_device, to_f64
 from test_gpu_prefill import CASES
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +45,7 @@ def test_ws_prefill_parity(case):
     (qb, kb, vb), out, lse = _run_ws(wid, b, n_q, n_kv, hq, hkv, big_l, w, base)
     ref = oracle.bifocal_three_pass(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb), big_l, w, base)
     assert_parity(out, ref["out"])
-    assert_parity(lse, ref["lse"], "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)
+    assert_parity(lse, ref["lse"], "lse", max_tol=lse_tol(ref["g"]), mean_tol=LSE_MEAN_TOL)
 
 
 def test_ws_workspace_reused_with_smaller_problem():
@@ -67,27 +67,3 @@ def test_ws_short_input_needs_no_workspace_and_is_plain():
     jl.jl_plain_prefill(q, k, v, out_p, None)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out_p.view(torch.int16))
-
-
-@pytest.mark.parametrize("name", ["qwen3_8b_128k", "qwen3_1p7b_64k"])
-def test_ws_full_size_sampled_rows(name):
-    wid, s, hq, hkv, big_l, w, base = FULL[name]
-    g = oracle.group_factor(s, big_l)
-    print(f"ws full size {name}: s={s} Hq={hq} Hkv={hkv} g={g}", flush=True)
-    qb, kb, vb = make_qkv(wid, 1, s, s, hq, hkv, 128)
-    q, k, v = to_device(qb), to_device(kb), to_device(vb)
-    out = torch.empty_like(q)
-    lse = torch.empty((1, hq, s), dtype=torch.float32, device="cuda:0")
-    ws = _workspace(1, s, hkv)
-    jl.jl_bifocal_prefill_ws(q, k, v, out, lse, big_l, w, base, ws)
-    torch.cuda.synchronize()
-    rows = sample_rows(s, s, big_l, w, g, count=20)
-    grp = hq // hkv
-    kf, vf = bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
-    for kvh in (0, hkv - 1):
-        heads = slice(kvh * grp, (kvh + 1) * grp)
-        ref = oracle.bifocal_three_pass(bf16_bits_to_f64(qb[:, :, heads]), kf[:, :, kvh:kvh + 1],
-                                        vf[:, :, kvh:kvh + 1], big_l, w, base, rows=rows)
-        assert_parity(to_f64(out[:, rows, heads]), ref["out"], f"{name} kv head {kvh}")
-        got_lse = lse[:, heads][:, :, rows].cpu().numpy().astype(np.float64)
-        assert_parity(got_lse, ref["lse"], "lse", max_tol=LSE_TOL, mean_tol=LSE_MEAN_TOL)

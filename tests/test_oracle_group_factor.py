@@ -1,7 +1,7 @@
 """Pins for the oracle's g(s) search (CPU only).
 
-The rule (ResearchPod summary, 2nd paragraph: the smallest integer grouping that
-keeps remote rotation angles in the pretrained distribution) is checked against
+The rule (ResearchPod summary, 2nd paragraph: distant positions are folded by the
+least integer factor that keeps them inside the trained range) is checked against
 the closed form ceil(s/L), against the range/minimality invariants it must
 satisfy, and against hand-worked values for every workload size.
 """

@@ -54,12 +54,12 @@ _i32, _i64, _f32, _f64, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_flo
 _SIGNATURES = {
     "jl_last_error": (ctypes.c_char_p, []),
     "jl_group_factor": (_i64, [_i64, _i64]),
-    "jl_bifocal_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
-                                  _f32, _vp]),
+    "jl_bifocal_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                  _f64, _f32, _vp]),
     "jl_bifocal_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "jl_bifocal_prefill_ws": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
                                      _f32, _vp, _sz, _vp]),
-    "jl_plain_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "jl_plain_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "jl_bifocal_prefill_passes": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
                                          _f64, _f32, _vp]),
     "jl_bifocal_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -147,13 +147,14 @@ def jl_group_factor(seq_len: int, pretrained_window: int) -> int:
 
 
 def jl_bifocal_prefill(q, k, v, out, lse, pretrained_window, local_window, rope_base,
-                       softmax_scale=0.0, stream=None):
-    """q [B, n_q, Hq, D], k/v [B, n_kv, Hkv, D] bf16; out like q; lse fp32 [B, Hq, n_q] or None."""
+                       softmax_scale=0.0, stream=None, q_pos=None):
+    """q [B, n_q, Hq, D], k/v [B, n_kv, Hkv, D] bf16; out like q; lse fp32 [B, Hq, n_q] or None;
+    q_pos None (the newest n_q positions) or an int32 device tensor [n_q] of query positions."""
     b, n_q, hq, d = q.shape
     n_kv, hkv = k.shape[1], k.shape[2]
-    _check(load_library().jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq,
-                                             hkv, d, int(pretrained_window), int(local_window), float(rope_base),
-                                             float(softmax_scale), _stream(stream)))
+    _check(load_library().jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _pos_ptr(q_pos), b,
+                                             n_q, n_kv, hq, hkv, d, int(pretrained_window), int(local_window),
+                                             float(rope_base), float(softmax_scale), _stream(stream)))
 
 
 def jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim=128) -> int:
@@ -172,11 +173,11 @@ def jl_bifocal_prefill_ws(q, k, v, out, lse, pretrained_window, local_window, ro
                                                 float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
 
 
-def jl_plain_prefill(q, k, v, out, lse, softmax_scale=0.0, stream=None):
+def jl_plain_prefill(q, k, v, out, lse, softmax_scale=0.0, stream=None, q_pos=None):
     b, n_q, hq, d = q.shape
     n_kv, hkv = k.shape[1], k.shape[2]
-    _check(load_library().jl_plain_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q, n_kv, hq, hkv,
-                                           d, float(softmax_scale), _stream(stream)))
+    _check(load_library().jl_plain_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _pos_ptr(q_pos), b, n_q,
+                                           n_kv, hq, hkv, d, float(softmax_scale), _stream(stream)))
 
 
 def jl_bifocal_prefill_passes(q, k, v, out_abc, lse_abc, pretrained_window, local_window, rope_base,
@@ -340,11 +341,11 @@ def jl_bifocal_prefill_varlen(q, k_cache, v_cache, out, lse, cu_seqlens_q, seq_l
                               local_window, rope_base, workspace, schedule="grouped", softmax_scale=0.0, stream=None):
     """q, out [total_q, Hq, D] packed rows; caches [B, max_seq_len, Hkv, D]; lse
     [Hq, total_q] or None; cu_seqlens_q int32 [B+1] and seq_lens int32 [B] on the
-    device; max_q >= every sequence's new rows; workspace as for
-    jl_bifocal_prefill_ws with n_kv = max_seq_len."""
+    device; max_q >= every sequence's new rows; workspace None (the single-kernel form)
+    or as for jl_bifocal_prefill_ws with n_kv = max_seq_len (the two-launch form)."""
     total_q, hq, d = q.shape
     b, n_max, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().jl_bifocal_prefill_varlen(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _cu_ptr(cu_seqlens_q), _seq_lens_ptr(seq_lens), b,
         total_q, int(max_q), n_max, hq, hkv, d, int(pretrained_window), int(local_window), float(rope_base),
@@ -361,6 +362,8 @@ def jl_plain_prefill_varlen(q, k_cache, v_cache, out, lse, cu_seqlens_q, seq_len
 
 
 def _pos_ptr(q_pos):
+    if q_pos is None:
+        return None
     import torch
     if q_pos.dtype != torch.int32:
         raise TypeError("q_pos must be an int32 device tensor")
@@ -369,8 +372,8 @@ def _pos_ptr(q_pos):
 
 def jl_bifocal_prefill_positions(q, k, v, out, lse, q_pos, pretrained_window, local_window, rope_base,
                                  workspace=None, schedule="grouped", softmax_scale=0.0, stream=None):
-    """As jl_bifocal_prefill_ws, with query row i at position q_pos[i] (int32 device
-    tensor [n_q], nondecreasing); the workspace may be None when g = 1."""
+    """Query row i at position q_pos[i] (int32 device tensor [n_q], nondecreasing), under
+    `schedule`; with a workspace the two-launch form, with workspace None the single kernel."""
     b, n_q, hq, d = q.shape
     n_kv, hkv = k.shape[1], k.shape[2]
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

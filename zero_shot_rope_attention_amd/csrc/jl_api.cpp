@@ -131,17 +131,26 @@ int64_t jl_group_factor(int64_t seq_len, int64_t pretrained_window) {
   return g < 1 ? 1 : g;
 }
 
-jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
-                           int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                           float softmax_scale, void* stream) {
+// Explicit query positions: NULL (the newest rows) or a 4-byte-aligned device array.
+static jl_status check_positions(const int32_t* q_pos, bool nullable) {
+  if (!q_pos) return nullable ? JL_OK : fail(JL_ERR_INVALID_ARG, "q_pos is NULL");
+  if (reinterpret_cast<uintptr_t>(q_pos) % 4 != 0) return fail(JL_ERR_INVALID_ARG, "q_pos is not 4-byte aligned");
+  return JL_OK;
+}
+
+jl_status jl_plain_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, float softmax_scale, void* stream) {
   float scale;
   const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
   JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
   JL_TRY(check_pointer(out, "out"));
   JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_positions(q_pos, true));
   JL_TRY(device_check());
   jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, 1,
                        2.0, scale};
+  p.q_pos = q_pos;
   return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -161,15 +170,16 @@ jl_status jl_sliding_prefill(const void* q, const void* k, const void* v, void* 
   return launched(jl::launch_prefill(jl::kModeSliding, p, static_cast<hipStream_t>(stream)));
 }
 
-jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t batch,
-                             int32_t n_q, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                             int64_t pretrained_window, int64_t local_window, double rope_base,
-                             float softmax_scale, void* stream) {
+jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window, int64_t local_window,
+                             double rope_base, float softmax_scale, void* stream) {
   float scale;
   const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
   JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
   JL_TRY(check_pointer(out, "out"));
   JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_positions(q_pos, true));
   JL_TRY(check_windows(pretrained_window, local_window, rope_base));
   JL_TRY(device_check());
   const int64_t g = jl_group_factor(n_kv, pretrained_window);
@@ -177,6 +187,7 @@ jl_status jl_bifocal_prefill(const void* q, const void* k, const void* v, void* 
   const jl::PrefillMode mode = g == 1 ? jl::kModePlain : jl::kModeBifocal;
   jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads,
                        (int32_t)g, w, rope_base, scale};
+  p.q_pos = q_pos;
   return launched(jl::launch_prefill(mode, p, static_cast<hipStream_t>(stream)));
 }
 
@@ -453,20 +464,26 @@ jl_status jl_bifocal_prefill_varlen(const void* q, const void* k_cache, const vo
   JL_TRY(check_pointer(lse, "lse", true));
   JL_TRY(check_windows(pretrained_window, local_window, rope_base));
   JL_TRY(check_schedule(schedule, pretrained_window, local_window, max_seq_len));
-  JL_TRY(check_pointer(workspace, "workspace"));
-  const size_t need = jl_bifocal_prefill_workspace_size(batch, max_seq_len, n_kv_heads, head_dim);
-  if (workspace_bytes < need) return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  // a workspace selects the two-launch form (corrected keys written first); none, the single kernel
+  const bool two_launch = workspace != nullptr || workspace_bytes != 0;
+  if (two_launch) {
+    JL_TRY(check_pointer(workspace, "workspace"));
+    const size_t need = jl_bifocal_prefill_workspace_size(batch, max_seq_len, n_kv_heads, head_dim);
+    if (workspace_bytes < need)
+      return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  }
   JL_TRY(device_check());
   // the factor, the shift and the rate are taken per sequence in the kernels
   const int32_t w = (int32_t)(local_window < max_seq_len ? local_window : max_seq_len);
-  jl::PrefillProblem p{q, k_cache, v_cache, out, lse, nullptr, nullptr, workspace, batch, max_q, max_seq_len,
-                       n_q_heads, n_kv_heads, 1, w, rope_base, scale};
+  jl::PrefillProblem p{q, k_cache, v_cache, out, lse, nullptr, nullptr, two_launch ? workspace : nullptr, batch,
+                       max_q, max_seq_len, n_q_heads, n_kv_heads, 1, w, rope_base, scale};
   p.cu_q = cu_seqlens_q;
   p.kv_lens = seq_lens;
   p.total_q = total_q;
   p.schedule = schedule;
   p.pretrained_window = pretrained_window;
-  return launched(jl::launch_prefill(jl::kModeBifocalPre, p, static_cast<hipStream_t>(stream)));
+  return launched(
+      jl::launch_prefill(two_launch ? jl::kModeBifocalPre : jl::kModeBifocal, p, static_cast<hipStream_t>(stream)));
 }
 
 jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
@@ -486,12 +503,6 @@ jl_status jl_plain_prefill_varlen(const void* q, const void* k_cache, const void
   return launched(jl::launch_prefill(jl::kModePlain, p, static_cast<hipStream_t>(stream)));
 }
 
-static jl_status check_positions(const int32_t* q_pos) {
-  if (!q_pos) return fail(JL_ERR_INVALID_ARG, "q_pos is NULL");
-  if (reinterpret_cast<uintptr_t>(q_pos) % 4 != 0) return fail(JL_ERR_INVALID_ARG, "q_pos is not 4-byte aligned");
-  return JL_OK;
-}
-
 jl_status jl_bifocal_prefill_positions(const void* q, const void* k, const void* v, void* out, float* lse,
                                        const int32_t* q_pos, int32_t batch, int32_t n_q, int32_t n_kv,
                                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -503,24 +514,27 @@ jl_status jl_bifocal_prefill_positions(const void* q, const void* k, const void*
   JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
   JL_TRY(check_pointer(out, "out"));
   JL_TRY(check_pointer(lse, "lse", true));
-  JL_TRY(check_positions(q_pos));
+  JL_TRY(check_positions(q_pos, false));
   JL_TRY(check_windows(pretrained_window, local_window, rope_base));
   JL_TRY(check_schedule(schedule, pretrained_window, local_window, n_kv));
   const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
   const int32_t g = jl::sched_group(n_kv, pretrained_window, w, schedule);
-  if (g > 1) {
+  // a workspace selects the two-launch form (corrected keys written first); none, the single kernel
+  const bool two_launch = workspace != nullptr || workspace_bytes != 0;
+  if (g > 1 && two_launch) {
     JL_TRY(check_pointer(workspace, "workspace"));
     const size_t need = jl_bifocal_prefill_workspace_size(batch, n_kv, n_kv_heads, head_dim);
     if (workspace_bytes < need)
       return fail(JL_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", workspace_bytes, need);
   }
   JL_TRY(device_check());
-  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, g > 1 ? workspace : nullptr, batch, n_q, n_kv,
-                       n_q_heads, n_kv_heads, g, w, rope_base, scale};
+  const jl::PrefillMode mode = g == 1 ? jl::kModePlain : (two_launch ? jl::kModeBifocalPre : jl::kModeBifocal);
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, mode == jl::kModeBifocalPre ? workspace : nullptr, batch,
+                       n_q, n_kv, n_q_heads, n_kv_heads, g, w, rope_base, scale};
   p.q_shift = jl::sched_q_shift(g, w, schedule);
   p.rate = jl::sched_rate(n_kv, pretrained_window, schedule);
   p.q_pos = q_pos;
-  return launched(jl::launch_prefill(g > 1 ? jl::kModeBifocalPre : jl::kModePlain, p, static_cast<hipStream_t>(stream)));
+  return launched(jl::launch_prefill(mode, p, static_cast<hipStream_t>(stream)));
 }
 
 jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -532,7 +546,7 @@ jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v
   JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
   JL_TRY(check_pointer(out, "out"));
   JL_TRY(check_pointer(lse, "lse", true));
-  JL_TRY(check_positions(q_pos));
+  JL_TRY(check_positions(q_pos, false));
   JL_TRY(device_check());
   jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads, 1, 1,
                        2.0, scale};
@@ -603,10 +617,11 @@ jl_status jl_plain_decode_paged(const void* q, const void* k_pages, const void* 
 }
 
 // Workspace of the attention layer: projected q/k/v, rotated queries, the
-// attention output, and the attention's own workspace (corrected keys for the
-// prefill, chunk partials for the decode), each 256-byte aligned.
+// attention output, the attention's own workspace (chunk partials for the
+// decode; the prefill needs none) and the library GEMM's scratch, each
+// 256-byte aligned.
 struct LayerWorkspace {
-  size_t qkv, q, attn, attn_ws, total;
+  size_t qkv, q, attn, attn_ws, gemm_ws, total;
 };
 static bool layer_workspace(int32_t batch, int32_t n_new, int32_t n_kv, int32_t hq, int32_t hkv, LayerWorkspace* l) {
   const int64_t e_qkv = elements(batch, n_new, (int64_t)hq + 2 * (int64_t)hkv);
@@ -617,9 +632,9 @@ static bool layer_workspace(int32_t batch, int32_t n_new, int32_t n_kv, int32_t 
   l->q = up((size_t)e_qkv * 2);
   l->attn = l->q + up((size_t)e_q * 2);
   l->attn_ws = l->attn + up((size_t)e_q * 2);
-  const size_t aw = n_new == 1 ? jl::decode_workspace_bytes(batch, n_kv, hq, hkv)
-                               : (size_t)elements(batch, n_kv, hkv) * 2;
-  l->total = l->attn_ws + up(aw);
+  const size_t aw = n_new == 1 ? jl::decode_workspace_bytes(batch, n_kv, hq, hkv) : 0;
+  l->gemm_ws = l->attn_ws + up(aw);
+  l->total = l->gemm_ws + jl::kGemmWorkspaceBytes;
   return true;
 }
 
@@ -679,12 +694,13 @@ jl_status jl_qwen3_attention_layer(const void* x, const void* w_qkv, const void*
   void* q = ws + l.q;
   void* attn = ws + l.attn;
   void* attn_ws = ws + l.attn_ws;
+  void* gemm_ws = ws + l.gemm_ws;
   const float scale = 1.0f / std::sqrt(128.0f);
   const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
   const int32_t g = bif_req ? jl::sched_group(n_kv, pretrained_window, w, schedule) : 1;
   const bool bif = bif_req && g > 1;
 
-  hipError_t e = jl::launch_gemm_xwt(x, w_qkv, qkv, t, n_qkv, hidden, st);
+  hipError_t e = jl::launch_gemm_xwt(x, w_qkv, qkv, t, n_qkv, hidden, gemm_ws, jl::kGemmWorkspaceBytes, st);
   if (e != hipSuccess) return launched(e);
   jl::NormRopeProblem nr{qkv, q_norm_weight, k_norm_weight, q, k_cache, v_cache, batch, n_new, n_kv, n_q_heads,
                          n_kv_heads, rms_eps, rope_base};
@@ -696,16 +712,18 @@ jl_status jl_qwen3_attention_layer(const void* x, const void* w_qkv, const void*
     p.schedule = bif ? schedule : jl::kSchedGrouped;
     e = jl::launch_decode(bif, p, st);
   } else {
-    jl::PrefillProblem p{q, k_cache, v_cache, attn, nullptr, nullptr, nullptr, bif ? attn_ws : nullptr, batch,
+    // the single-kernel bifocal prefill: keys corrected in LDS, no workspace
+    jl::PrefillProblem p{q, k_cache, v_cache, attn, nullptr, nullptr, nullptr, nullptr, batch,
                          n_new, n_kv, n_q_heads, n_kv_heads, bif ? g : 1, bif ? w : 1, rope_base, scale};
     if (bif) {
       p.q_shift = jl::sched_q_shift(g, w, schedule);
       p.rate = jl::sched_rate(n_kv, pretrained_window, schedule);
     }
-    e = jl::launch_prefill(bif ? jl::kModeBifocalPre : jl::kModePlain, p, st);
+    e = jl::launch_prefill(bif ? jl::kModeBifocal : jl::kModePlain, p, st);
   }
   if (e != hipSuccess) return launched(e);
-  return launched(jl::launch_gemm_xwt(attn, w_o, out, t, hidden, (int64_t)n_q_heads * 128, st));
+  return launched(
+      jl::launch_gemm_xwt(attn, w_o, out, t, hidden, (int64_t)n_q_heads * 128, gemm_ws, jl::kGemmWorkspaceBytes, st));
 }
 
 }  // extern "C"

@@ -348,8 +348,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
             const float co = __builtin_amdgcn_cosf(rev);
             const float si = __builtin_amdgcn_sinf(rev);
             const float x1 = elem(kr[kk], e), x2 = elem(kr[kk + 4], e);
-            y1[q2] = x1 * co - x2 * si;
-            y2[q2] = x2 * co + x1 * si;
+            const f32x2 yr = rot_pair(x1, x2, co, si);
+            y1[q2] = yr.x;
+            y2[q2] = yr.y;
           }
           lo[e2] = pack_bf16(y1[0], y1[1]);
           hi[e2] = pack_bf16(y2[0], y2[1]);
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i2], a.scale_log2, mc));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i2 + 1], a.scale_log2, mc));
       pk[i2] = pack_bf16(p0, p1);
-      psum = add_bf16_pair(pk[i2], psum);
+      psum += p0 + p1;  // fp32 probabilities: the normaliser carries fp32 rounding only
     }
     l_run += psum;
     // O^T += V^T P^T: keys 16h + 8half + e

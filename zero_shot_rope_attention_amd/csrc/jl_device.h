@@ -64,10 +64,17 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
                                          acc, false);
 }
 
-// Complex product (a.x + i a.y)(b.x + i b.y).
-__device__ __forceinline__ f32x2 cmul(f32x2 a, f32x2 b) {
-  return f32x2{a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x};
+// Rotation of the rotate-half pair (x1, x2) by the angle with cosine c and sine
+// s: (x1 c - x2 s, x2 c + x1 s).  Each component is one explicit fused
+// multiply-add over one rounded product, so every kernel rounds it the same way
+// whatever the compiler would contract on its own.
+__device__ __forceinline__ f32x2 rot_pair(float x1, float x2, float c, float s) {
+  return f32x2{__builtin_fmaf(x1, c, -(x2 * s)), __builtin_fmaf(x2, c, x1 * s)};
 }
+
+// Complex product (a.x + i a.y)(b.x + i b.y), rounded as rot_pair (the same
+// rotation written on the first factor).
+__device__ __forceinline__ f32x2 cmul(f32x2 a, f32x2 b) { return rot_pair(a.x, a.y, b.x, b.y); }
 
 // Direct HBM -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
 // lane l's 16 bytes land at lds_wave_base + 16 l; lds_wave_base must be the

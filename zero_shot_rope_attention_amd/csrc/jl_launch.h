@@ -135,8 +135,11 @@ struct NormRopeProblem {
 };
 hipError_t launch_norm_rope(const NormRopeProblem& p, hipStream_t stream);
 
-// Row-major y[m, n] = x[m, k] w[n, k]^T in bf16 with fp32 accumulation (rocBLAS).
+// Row-major y[m, n] = x[m, k] w[n, k]^T in bf16 with fp32 accumulation: the
+// library's weight-streaming kernel for up to 8 rows, rocBLAS otherwise, whose
+// scratch is gemm_ws (kGemmWorkspaceBytes of device memory from the caller).
+constexpr size_t kGemmWorkspaceBytes = size_t(32) << 20;
 hipError_t launch_gemm_xwt(const void* x, const void* w, void* y, int64_t m, int64_t n, int64_t k,
-                           hipStream_t stream);
+                           void* gemm_ws, size_t gemm_ws_bytes, hipStream_t stream);
 
 }  // namespace jl

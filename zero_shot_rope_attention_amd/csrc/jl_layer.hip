@@ -167,15 +167,24 @@ hipError_t launch_gemv(const void* x, const void* w, void* y, int n, int k, hipS
   return hipGetLastError();
 }
 
-// rocBLAS handle of the calling thread for the current device (created on
-// first use and kept until the process ends).
+// rocBLAS handles of the calling thread, one per device: created on first use,
+// destroyed when the thread exits.
+struct ThreadHandles {
+  static constexpr int kMaxDevices = 64;
+  rocblas_handle h[kMaxDevices] = {};
+  ~ThreadHandles() {
+    for (rocblas_handle& x : h)
+      if (x) rocblas_destroy_handle(x);
+  }
+};
+
 rocblas_handle thread_handle() {
-  constexpr int kMaxDevices = 64;
-  thread_local rocblas_handle handles[kMaxDevices] = {};
+  thread_local ThreadHandles handles;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) handles[dev] = nullptr;
-  return handles[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= ThreadHandles::kMaxDevices) return nullptr;
+  rocblas_handle& h = handles.h[dev];
+  if (!h && rocblas_create_handle(&h) != rocblas_status_success) h = nullptr;
+  return h;
 }
 
 }  // namespace
@@ -207,7 +216,7 @@ hipError_t launch_norm_rope(const NormRopeProblem& p, hipStream_t stream) {
 // In rocBLAS's column-major terms that is y^T (n x m) = w (op T of the k x n
 // column-major view) times x^T (k x m).
 hipError_t launch_gemm_xwt(const void* x, const void* w, void* y, int64_t m, int64_t n, int64_t k,
-                           hipStream_t stream) {
+                           void* gemm_ws, size_t gemm_ws_bytes, hipStream_t stream) {
   if (m == 0) return hipSuccess;
   if (m > 0x7fffffff || n > 0x7fffffff || k > 0x7fffffff) return hipErrorInvalidValue;
   // a few tokens (decode): the weight-streaming kernel above; 16-byte rows need k % 8 == 0
@@ -227,6 +236,8 @@ hipError_t launch_gemm_xwt(const void* x, const void* w, void* y, int64_t m, int
   rocblas_handle h = thread_handle();
   if (!h) return hipErrorInvalidValue;
   if (rocblas_set_stream(h, stream) != rocblas_status_success) return hipErrorInvalidValue;
+  // the GEMM's scratch is the caller's memory: rocBLAS allocates none for it
+  if (rocblas_set_workspace(h, gemm_ws, gemm_ws_bytes) != rocblas_status_success) return hipErrorInvalidValue;
   const float alpha = 1.0f, beta = 0.0f;
   const rocblas_status st =
       rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)n, (rocblas_int)m,

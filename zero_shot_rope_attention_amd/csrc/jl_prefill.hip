@@ -201,8 +201,9 @@ __device__ __forceinline__ void store_k(const KRegs<512 / NT>& r, uint8_t* sk, u
         const int e = 2 * e2 + q2;
         const f32x2 cs = cmul(bs[e], td[e]);
         const float x1 = elem(r.lo[it], e), x2 = elem(r.hi[it], e);
-        y1[q2] = x1 * cs.x - x2 * cs.y;
-        y2[q2] = x2 * cs.x + x1 * cs.y;
+        const f32x2 yr = rot_pair(x1, x2, cs.x, cs.y);
+        y1[q2] = yr.x;
+        y2[q2] = yr.y;
       }
       glo[e2] = pack_bf16(y1[0], y1[1]);
       ghi[e2] = pack_bf16(y2[0], y2[1]);
@@ -307,10 +308,14 @@ __device__ __forceinline__ void softmax_max(const float (&x)[NS][2][16], float (
   }
 }
 
-// Online softmax, second half: probabilities (bf16 pairs) and row sums.  The
-// sums add the bf16-rounded probabilities, the same values the P V product
-// weights the rows of V with, so the normalised weights sum to one.
-template <int NS>
+// Online softmax, second half: probabilities (bf16 pairs) and row sums.
+// kF32Sum: the sums add the fp32 probabilities, so the normaliser (and the lse)
+// carry fp32 rounding only.  Otherwise they add the bf16-rounded probabilities,
+// the weights the P V product applies, in one v_dot2 per pair (fewer VALU
+// instructions, which the single-kernel bifocal mode is bound by); the lse then
+// carries the probabilities' bf16 rounding, a relative error of at most 2^-8 in
+// the normaliser.
+template <int NS, bool kF32Sum>
 __device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const float (&m_run)[NS],
                                             float (&l_run)[NS], float scale_log2, uint32_t (&pk)[NS][2][8]) {
 #pragma unroll
@@ -324,7 +329,8 @@ __device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const f
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[s][kb][2 * i2], scale_log2, mc));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[s][kb][2 * i2 + 1], scale_log2, mc));
         pk[s][kb][i2] = pack_bf16(p0, p1);
-        psum = add_bf16_pair(pk[s][kb][i2], psum);
+        if constexpr (kF32Sum) psum += p0 + p1;
+        else psum = add_bf16_pair(pk[s][kb][i2], psum);
       }
     }
     l_run[s] += psum;
@@ -463,8 +469,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
             const int d = 16 * kk + 8 * h + e;
             const f32x2 cs = rot_cs(cq, a.theta_rev[d]);
             const float x1 = elem(raw[kk], e), x2 = elem(raw[kk + 4], e);
-            y1[t] = x1 * cs.x - x2 * cs.y;
-            y2[t] = x2 * cs.x + x1 * cs.y;
+            const f32x2 yr = rot_pair(x1, x2, cs.x, cs.y);
+            y1[t] = yr.x;
+            y2[t] = yr.y;
           }
           lo[e2] = pack_bf16(y1[0], y1[1]);
           hi[e2] = pack_bf16(y2[0], y2[1]);
@@ -567,7 +574,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
     // region 1: QK MFMAs of tile t+1 beside the exponentials of tile t
     uint32_t pk[NS][2][8];
     if (kNextInterior || (t + 1 < ntiles && wave_uses(t + 1))) scores(t + 1, next_interior_tag, x_next);
-    if (act) softmax_exp<NS>(x_cur, m_run, l_run, a.scale_log2, pk);
+    if (act) softmax_exp<NS, true>(x_cur, m_run, l_run, a.scale_log2, pk);
     __builtin_amdgcn_sched_barrier(0);
     // region 2: PV MFMAs of tile t beside the staging of tile t+2
     if (act) pv_tile<NS>(s_v + (t % 3) * kTileBytes, lofs, pk, acc);
@@ -743,8 +750,9 @@ __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8
         const int e = 2 * e2 + q2;
         const f32x2 cs = cmul(bs[e], td[e]);
         const float x1 = elem(r.klo, e), x2 = elem(r.khi, e);
-        y1[q2] = x1 * cs.x - x2 * cs.y;
-        y2[q2] = x2 * cs.x + x1 * cs.y;
+        const f32x2 yr = rot_pair(x1, x2, cs.x, cs.y);
+        y1[q2] = yr.x;
+        y2[q2] = yr.y;
       }
       glo[e2] = pack_bf16(y1[0], y1[1]);
       ghi[e2] = pack_bf16(y2[0], y2[1]);
@@ -819,8 +827,8 @@ template <int MODE, bool VARLEN = false, bool QPOS = false>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
   static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre || MODE == kModeSliding,
                 "ping-pong kernel: plain, bifocal or sliding window");
-  static_assert(!(VARLEN || QPOS) || MODE == kModePlain || MODE == kModeBifocalPre,
-                "variable-length batches and explicit positions: plain, or bifocal with corrected keys staged");
+  static_assert(!(VARLEN || QPOS) || MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre,
+                "variable-length batches and explicit positions: plain or bifocal");
   static_assert(!(VARLEN && QPOS), "explicit positions are for uniform batches");
   constexpr bool kSliding = MODE == kModeSliding;   // base scores on the window's keys only
   constexpr bool kGrouped = MODE != kModePlain && !kSliding;  // grouped scores on remote keys
@@ -833,6 +841,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];                  // V row-major
   __shared__ f32x2 s_tdelta[kRotate ? 64 * kTdStride : 1];  // E(-u theta_d), u = 0..63, padded rows
   __shared__ f32x2 s_base[kRotate ? 4 * kHalfD : 1];     // E(c(j0) theta_d): [group][parity of k]
+  __shared__ double s_theta[kRotate ? kHalfD : 1];       // theta_d / (2 pi) of this sequence
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -865,7 +874,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     sv.n_q = min(min(max(a.cu_q[bv + 1] - sv.q0, 0), a.total_q - sv.q0), min(a.n_q, sv.n_kv));
     sv.n_qblocks = (sv.n_q + a.bm - 1) / a.bm;
     if (rank >= sv.n_qblocks) return;  // a shorter sequence: no query block here
-    if constexpr (MODE == kModeBifocalPre) {
+    if constexpr (MODE == kModeBifocal || MODE == kModeBifocalPre) {
       sv.g = sched_group(sv.n_kv, a.big_l, a.w, a.sched);
       sv.q_shift = sched_q_shift(sv.g, a.w, a.sched);
       sv.rate = sched_rate(sv.n_kv, a.big_l, a.sched);
@@ -931,11 +940,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   auto k_src = [&](int t) { return (kPre && t < n_interior) ? kgbase : kbase; };
   auto k_dst = [&](int t) { return ((kPre && t < n_interior) ? s_kg : s_k) + (t & 1) * kTileBytes; };
 
-  // rotation table first, while few values are live
+  // rotation table first, while few values are live; theta_d is kept in LDS for
+  // the per-tile base angles (a load from the argument block inside the loop
+  // would put its latency on every tile's VALU phase)
   if constexpr (kRotate) {
+    if (tid < kHalfD) s_theta[tid] = SEQ_THETA(tid);
 #pragma unroll 1
     for (int idx = tid; idx < 64 * kHalfD; idx += 512)
-      s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), a.theta_rev[idx & 63]);
+      s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), SEQ_THETA(idx & 63));
   }
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
@@ -964,8 +976,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
             const int e = 2 * e2 + t;
             const f32x2 cs = rot_cs(cq, SEQ_THETA(16 * kk + 8 * h + e));
             const float x1 = elem(raw[kk], e), x2 = elem(raw[kk + 4], e);
-            y1[t] = x1 * cs.x - x2 * cs.y;
-            y2[t] = x2 * cs.x + x1 * cs.y;
+            const f32x2 yr = rot_pair(x1, x2, cs.x, cs.y);
+            y1[t] = yr.x;
+            y2[t] = yr.y;
           }
           lo[e2] = pack_bf16(y1[0], y1[1]);
           hi[e2] = pack_bf16(y2[0], y2[1]);
@@ -978,8 +991,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 
   auto base_angles = [&](int tt, int slot) {  // by the first 64 threads of a group
     const int j = min(tt, ntiles - 1) * kBN;
-    s_base[slot * kHalfD + (gtid & 63)] = rot_cs((long long)(j / a.g) - j, a.theta_rev[gtid & 63]);
+    s_base[slot * kHalfD + (gtid & 63)] = rot_cs((long long)(j / SEQ_G) - j, s_theta[gtid & 63]);
   };
+  const float inv_g = VARLEN ? 1.0f / (float)sv.g : a.inv_g;
   auto store = [&](int tt, int slot) {  // slot: rotation-base slot
     if constexpr (kPre) {
       store_half<false>(regs, k_dst(tt), nullptr, s_v + (tt % 3) * kTileBytes, nullptr, nullptr, 0, 1, 1.0f, grp,
@@ -992,7 +1006,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     } else {
       store_half<kRotate>(regs, s_k + (tt & 1) * kTileBytes, s_kg + (kRotate ? (tt & 1) * kTileBytes : 0),
                           s_v + (tt % 3) * kTileBytes, s_tdelta, s_base + (kRotate ? slot * kHalfD : 0), tt * kBN,
-                          a.g, a.inv_g, grp, gtid);
+                          SEQ_G, inv_g, grp, gtid);
     }
   };
 
@@ -1001,7 +1015,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   // stages in V(k); the prologue borrows slot [grp][0] for tiles 0 and 1.
   if constexpr (kRotate) {
     if (gtid < 64) {
-      s_base[(2 * grp) * kHalfD + gtid] = rot_cs(0, a.theta_rev[gtid]);  // tile 0: c(0) = 0
+      s_base[(2 * grp) * kHalfD + gtid] = f32x2{1.0f, 0.0f};  // tile 0: c(0) = 0
     }
     __syncthreads();
   }
@@ -1108,7 +1122,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || kKind == kLocalFree || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
-      softmax_exp<1>(xs, m_run, l_run, a.scale_log2, pk);
+      softmax_exp<1, !kRotate>(xs, m_run, l_run, a.scale_log2, pk);
     }
     // the scores are dead once the probabilities exist: keep the staging after
     __builtin_amdgcn_sched_barrier(0);
@@ -1237,8 +1251,9 @@ __global__ __launch_bounds__(256) void correct_keys_kernel(const CorrectArgs a) 
       for (int q2 = 0; q2 < 2; ++q2) {
         const int e = 2 * e2 + q2;
         const float x1 = elem(lo, e), x2 = elem(hi, e);
-        y1[q2] = x1 * cs[e].x - x2 * cs[e].y;
-        y2[q2] = x2 * cs[e].x + x1 * cs[e].y;
+        const f32x2 yr = rot_pair(x1, x2, cs[e].x, cs[e].y);
+        y1[q2] = yr.x;
+        y2[q2] = yr.y;
       }
       glo[e2] = pack_bf16(y1[0], y1[1]);
       ghi[e2] = pack_bf16(y2[0], y2[1]);
@@ -1285,7 +1300,8 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   a.sched = p.schedule;
   a.big_l = p.pretrained_window;
   a.q_pos = p.q_pos;
-  if ((p.cu_q || p.q_pos) && !(MODE == kModePlain || MODE == kModeBifocalPre)) return hipErrorInvalidValue;
+  if ((p.cu_q || p.q_pos) && !(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre))
+    return hipErrorInvalidValue;
   if (p.cu_q && p.q_pos) return hipErrorInvalidValue;
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   // theta_d / (2 pi), times the schedule's rate (1 but for the fractional one)
@@ -1316,7 +1332,7 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   }
   if constexpr (MODE == kModePasses)
     hipLaunchKernelGGL((prefill_kernel<MODE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
-  else if constexpr (MODE == kModePlain || MODE == kModeBifocalPre) {
+  else if constexpr (MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre) {
     if (p.cu_q)
       hipLaunchKernelGGL((prefill_pp_kernel<MODE, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
     else if (p.q_pos)
