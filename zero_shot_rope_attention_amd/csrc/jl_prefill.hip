@@ -769,10 +769,17 @@ __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8
 // LDS operands of step i+3 are read while the MFMAs of step i run (a ring of 4
 // operand sets), and the order is pinned so the compiler does not hoist all 48
 // reads ahead of the matrix work.
-template <bool kPV>
+// `hook(i)` runs at step i = 0..15 (a constant once unrolled), in the same
+// scheduling region as that step's two MFMAs, so the work it adds issues in
+// the matrix cores' shadow.
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <bool kPV, typename Hook = NoHook>
 __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8_t* vbuf, const LaneOffsets& lo,
                                                 const bf16x8 (&q)[8], const uint32_t (&pk)[1][2][8],
-                                                f32x16 (&sc)[2], f32x16 (&acc)[1][4]) {
+                                                f32x16 (&sc)[2], f32x16 (&acc)[1][4], const Hook& hook = Hook()) {
   constexpr int kDist = 2;
   auto read_k = [&](int i) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(kbuf + lo.k[i >> 1] + (i & 1) * (32 * 256));
@@ -810,6 +817,7 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
                         pk[0][kb][4 * half + 3]};
       acc[0][nb] = mfma32(as_bf16x8(vr[i % (kDist + 1)]), as_bf16x8(pf), acc[0][nb]);
     }
+    hook(i);
     __builtin_amdgcn_sched_barrier(0);
   }
   sc[0] = s0;
@@ -1192,6 +1200,366 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-kernel bifocal prefill: the keys are corrected tile by tile in LDS.
+//
+// The ping-pong of prefill_pp_kernel (waves 0-3 and 4-7 half a tile apart, one
+// group in its MFMA phase while the other is in its VALU phase), with the
+// staging of the next key tile moved into the MFMA phase: the correction
+// rotation of its keys, its LDS writes, the loads of the tile after it and that
+// tile's rotation base are spread over the steps of the MFMA sequence, and the
+// VALU phase keeps the softmax only.  A wave issues about one instruction per
+// 4-5 cycles whatever its kind, so a VALU phase holding both the softmax and
+// the rotation outlasts the other group's MFMA phase, whose wave leaves most of
+// its own issue slots idle between MFMAs.
+//
+// Tile program of each group for tile k:
+//   M(k): S = K^g Q^T of tile k and O^T += V^T P^T of tile k-1 (MFMA), and the
+//         group's half of tile k+1 into LDS (corrected keys, the keys as cached
+//         for band tiles, values), then the loads of its half of tile k+2 and
+//         that tile's rotation base.
+//   V(k): the softmax of tile k.
+// Tile k+1 is written in M(k) by both groups, into the K / K^g buffer of tile
+// k-1 and the V buffer of tile k-2, all last read in M(k-1) of both groups;
+// rotation bases sit in two slots per group (tile & 1): tile k+2's is written
+// at the end of M(k), after the staging of tile k+1 has read its own.  Staging past the last tile re-stages the
+// last one into slots no later phase reads, so the loop has no branches.
+// ---------------------------------------------------------------------------
+template <bool VARLEN = false, bool QPOS = false>
+__global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs a) {
+  static_assert(!(VARLEN && QPOS), "explicit positions are for uniform batches");
+  constexpr int kTileBytes = kBN * 256;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];     // K as cached (band tiles)
+  __shared__ __attribute__((aligned(16))) uint8_t s_kg[2 * kTileBytes];    // corrected K
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];     // V row-major
+  __shared__ __attribute__((aligned(16))) f32x2 s_tdelta[64 * kTdStride];  // E(-u theta_d), u < 64
+  __shared__ __attribute__((aligned(16))) f32x2 s_base[4 * kHalfD];        // E(c(j0) theta_d): [group][tile & 1]
+  __shared__ double s_theta[kHalfD];                                        // theta_d / (2 pi)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int gtid = tid & 255;
+  const int h = lane >> 5;
+
+  int unit, rank;
+  {
+    const int id = blockIdx.x;
+    if ((a.n_units & 7) == 0) {
+      const int slot = id >> 3;
+      unit = (id & 7) + 8 * (slot / a.n_qblocks);
+      rank = slot % a.n_qblocks;
+    } else {
+      unit = id / a.n_qblocks;
+      rank = id % a.n_qblocks;
+    }
+  }
+  SeqView sv{};
+  if constexpr (VARLEN) {
+    const int bv = unit / (a.grp / a.hpw) / a.hkv;
+    sv.n_kv = min(max(a.kv_lens[bv], 1), a.n_kv);
+    sv.q0 = min(max(a.cu_q[bv], 0), a.total_q);
+    sv.n_q = min(min(max(a.cu_q[bv + 1] - sv.q0, 0), a.total_q - sv.q0), min(a.n_q, sv.n_kv));
+    sv.n_qblocks = (sv.n_q + a.bm - 1) / a.bm;
+    if (rank >= sv.n_qblocks) return;  // a shorter sequence: no query block here
+    sv.g = sched_group(sv.n_kv, a.big_l, a.w, a.sched);
+    sv.q_shift = sched_q_shift(sv.g, a.w, a.sched);
+    sv.rate = sched_rate(sv.n_kv, a.big_l, a.sched);
+  }
+  const int qb = (VARLEN ? sv.n_qblocks : a.n_qblocks) - 1 - rank;
+  const int n_hg = a.grp / a.hpw;
+  const int hg = unit % n_hg;
+  const int bk = unit / n_hg;
+  const int kvh = bk % a.hkv;
+  const int b = bk / a.hkv;
+  const int hq = kvh * a.grp + hg * a.hpw + (wave % a.hpw);
+  const int row0_wg = qb * a.bm;
+  const int row0 = row0_wg + (wave / a.hpw) * 32;
+  const int pos_off = SEQ_N_KV - SEQ_N_Q;
+  const int last_row_wg = min(SEQ_N_Q, row0_wg + a.bm) - 1;
+  const int kend = QPOS ? SEQ_POS(last_row_wg) + 1 : pos_off + last_row_wg + 1;
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  const bool wave_rows = row0 < SEQ_N_Q;
+  const int wp_lo = QPOS ? SEQ_POS(min(row0, SEQ_N_Q - 1)) : pos_off + row0;
+  const int wp_hi = QPOS ? SEQ_POS(min(SEQ_N_Q, row0 + 32) - 1) : pos_off + min(SEQ_N_Q, row0 + 32) - 1;
+  const int my_row = row0 + (lane & 31);
+  const bool row_ok = my_row < SEQ_N_Q;
+  const int my_p = row_ok ? (QPOS ? SEQ_POS(my_row) : pos_off + my_row) : -1;
+  const int w = a.w;
+  const int g = SEQ_G;
+  const float inv_g = VARLEN ? 1.0f / (float)sv.g : a.inv_g;
+  const float scale_log2 = a.scale_log2;
+
+  const int64_t q_rs = (int64_t)a.hq * kD;
+  const int64_t kv_rs = (int64_t)a.hkv * kD;
+  const int n_kv = SEQ_N_KV;
+  const uint16_t* kbase = a.k + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+  const uint16_t* vbase = a.v + (int64_t)b * a.n_kv * kv_rs + (int64_t)kvh * kD;
+
+  // tile kinds: interior (every key remote for every row of the workgroup:
+  // grouped scores, no masks), edge (both score kinds), local (every causal key
+  // local for every row: base scores with the causal mask)
+  const int p0_wg = QPOS ? SEQ_POS(row0_wg) : pos_off + row0_wg;
+  const int n_interior = min(ntiles, max(0, (p0_wg - w + 1) / kBN));
+  int t_local;
+  {
+    const int first_all_local = (QPOS ? SEQ_POS(last_row_wg) : pos_off + last_row_wg) - w + 1;
+    t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
+    t_local = min(ntiles, max(n_interior, t_local));
+  }
+
+  // tables first, while few values are live
+  if (tid < kHalfD) s_theta[tid] = SEQ_THETA(tid);
+#pragma unroll 1
+  for (int idx = tid; idx < 64 * kHalfD; idx += 512)
+    s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), SEQ_THETA(idx & 63));
+
+  HalfTile regs;
+  const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
+  load_half(regs, kbase, vbase, kv_rs, n_kv, 0, soff);
+
+  bf16x8 qf[8];
+  bf16x8 qg[8];
+  {
+    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+    u32x4 raw[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      raw[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
+      qf[kk] = as_bf16x8(raw[kk]);
+    }
+    const long long cq = row_ok ? (long long)(my_p / g) - my_p + SEQ_Q_SHIFT : 0;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int e = 2 * e2 + t;
+          const f32x2 cs = rot_cs(cq, SEQ_THETA(16 * kk + 8 * h + e));
+          const f32x2 yr = rot_pair(elem(raw[kk], e), elem(raw[kk + 4], e), cs.x, cs.y);
+          y1[t] = yr.x;
+          y2[t] = yr.y;
+        }
+        lo[e2] = pack_bf16(y1[0], y1[1]);
+        hi[e2] = pack_bf16(y2[0], y2[1]);
+      }
+      qg[kk] = as_bf16x8(lo);
+      qg[kk + 4] = as_bf16x8(hi);
+    }
+  }
+
+  // ---- staging of this group's half of tile tt: 13 steps, run one per MFMA
+  // step of an interior tile's MFMA phase, or back to back otherwise: the
+  // corrected keys, the LDS writes, then the loads of the next tile and its
+  // rotation base ----
+  // this thread: key kt of the tile, rotate-half pairs 8c .. 8c+7
+  const int kt = 32 * grp + half_tile_key(gtid);
+  const int kc = half_tile_chunk(gtid);
+  // LDS byte offsets of this thread's staging writes, recomputed where they are
+  // used (a few VALU) rather than kept live through the loop
+  auto k_off = [&](int hi) {
+    int t = gtid;
+    asm volatile("" : "+v"(t));
+    const int key = 32 * grp + half_tile_key(t);
+    return key * 256 + (k_chunk(key, half_tile_chunk(t) + 8 * hi) << 4);
+  };
+  auto v_off = [&](int hi) {
+    int t = gtid;
+    asm volatile("" : "+v"(t));
+    const int row = 32 * grp + (t >> 4) + 16 * hi;
+    return row * 256 + (v_chunk(row, t & 15) << 4);
+  };
+  const f32x2* td = s_tdelta;
+  f32x2 tdr[2], bsr[2];
+  float ylo[2], yhi[2];
+  u32x4 glo, ghi;
+  const uint32_t ug = (uint32_t)g;  // positions are >= 0: unsigned division, fewer scalar steps
+  auto base_angles = [&](int tt) {  // by the group's first 64 threads
+    const uint32_t j = (uint32_t)(min(tt, ntiles - 1) * kBN);
+    s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rot_cs((long long)(j / ug) - (long long)j, s_theta[gtid]);
+  };
+  // kRot: tile tt needs corrected keys; kCached: it needs the keys as cached
+  auto stage_step = [&](int tt, int i, auto rot_tag, auto cached_tag) {
+    constexpr bool kRot = decltype(rot_tag)::value, kCached = decltype(cached_tag)::value;
+    const int ts = min(tt, ntiles - 1);  // past the last tile: the last one again, into unread slots
+    if constexpr (kRot) {
+      if (i == 0) {
+        // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g
+        const int u = kt - small_div((int)((uint32_t)(ts * kBN) % ug) + kt, g, inv_g);
+        td = s_tdelta + u * kTdStride + 8 * kc;
+      }
+      const f32x2* bs = s_base + (2 * grp + (tt & 1)) * kHalfD + 8 * kc;
+      auto issue = [&](int e) {
+        tdr[e & 1] = td[e];
+        bsr[e & 1] = bs[e];
+      };
+      if (i == 0) {
+        issue(0);
+        issue(1);
+      }
+      if (i >= 1 && i <= 8) {  // pair e = i - 1; the reads of pair e + 2 follow it
+        const int e = i - 1;
+        const f32x2 cs = cmul(bsr[e & 1], tdr[e & 1]);
+        const f32x2 yr = rot_pair(elem(regs.klo, e), elem(regs.khi, e), cs.x, cs.y);
+        ylo[e & 1] = yr.x;
+        yhi[e & 1] = yr.y;
+        if (e & 1) {
+          glo[e >> 1] = pack_bf16(ylo[0], ylo[1]);
+          ghi[e >> 1] = pack_bf16(yhi[0], yhi[1]);
+        }
+        if (e + 2 < 8) issue(e + 2);
+      }
+      if (i == 9) {
+        uint8_t* skg = s_kg + (tt & 1) * kTileBytes;
+        *reinterpret_cast<u32x4*>(skg + k_off(0)) = glo;
+        *reinterpret_cast<u32x4*>(skg + k_off(1)) = ghi;
+      }
+    }
+    if constexpr (kCached) {
+      if (i == 9) {
+        uint8_t* sk = s_k + (tt & 1) * kTileBytes;
+        *reinterpret_cast<u32x4*>(sk + k_off(0)) = regs.klo;
+        *reinterpret_cast<u32x4*>(sk + k_off(1)) = regs.khi;
+      }
+    }
+    if (i == 10) {
+      uint8_t* sv = s_v + (tt % 3) * kTileBytes;
+      *reinterpret_cast<u32x4*>(sv + v_off(0)) = regs.v0;
+      *reinterpret_cast<u32x4*>(sv + v_off(1)) = regs.v1;
+    }
+    if (i == 11) load_half(regs, kbase, vbase, kv_rs, n_kv, min(tt + 1, ntiles - 1) * kBN, soff);
+    if (i == 12 && gtid < 64) base_angles(tt + 1);
+  };
+  constexpr int kStageSteps = 13;
+  using TT = std::true_type;
+  using FF = std::false_type;
+
+  // ---- prologue: tile 0 staged, the loads and rotation base of tile 1 issued ----
+  __syncthreads();  // theta table
+  if (gtid < 64) base_angles(0);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kStageSteps; ++i) {
+    if (n_interior > 0) stage_step(0, i, TT{}, FF{});
+    else if (t_local > 0) stage_step(0, i, TT{}, TT{});
+    else stage_step(0, i, FF{}, TT{});
+  }
+
+  const LaneOffsets lofs = lane_offsets(lane);
+  float m_run[1] = {kNegBig}, l_run[1] = {0.0f};
+  f32x16 acc[1][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[0][nb] = f32x16{};
+  auto uses = [&](int t) { return wave_rows && t * kBN <= wp_hi; };
+  float xs[1][2][16];
+  uint32_t pk[1][2][8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk[0][kb][i] = 0u;
+
+  __syncthreads();
+  if (grp == 1) __syncthreads();  // group B runs one phase behind
+
+  constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
+  // tile k of kind KK, staging tile k + 1 of kind KT
+  auto tile = [&](int k, auto kk_tag, auto kt_tag) {
+    constexpr int KK = decltype(kk_tag)::value, KT = decltype(kt_tag)::value;
+    using RotT = std::integral_constant<bool, KT != kLocal>;
+    using CachedT = std::integral_constant<bool, KT != kInterior>;
+    __builtin_amdgcn_s_setprio(2);
+    const uint8_t* sk = s_k + (k & 1) * kTileBytes;
+    const uint8_t* skg = s_kg + (k & 1) * kTileBytes;
+    // V of tile k-1 (at tile 0 the probabilities are zero and tile 0's finite V is read)
+    const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) % 3) * kTileBytes;
+    if constexpr (KK == kInterior) {
+      f32x16 sc[2];
+      auto hook = [&](int i) {
+        if (i < kStageSteps) stage_step(k + 1, i, RotT{}, CachedT{});
+      };
+      mphase_interior<true>(skg, svp, lofs, qg, pk, sc, acc, hook);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[0][kb][i] = sc[kb][i];
+    } else {
+      const int j0 = k * kBN;
+      if (uses(k)) {
+        if constexpr (KK == kEdge) {
+          const bool use_grp = j0 <= wp_hi - w;
+          const bool use_base = j0 + kBN - 1 >= wp_lo - w + 1;
+          tile_scores<kModeBifocal, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, w, use_base, use_grp, xs);
+        } else {
+          tile_scores<kModePlain, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, w, true, false, xs);
+        }
+      }
+      if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
+#pragma unroll
+      for (int i = 0; i < kStageSteps; ++i) stage_step(k + 1, i, RotT{}, CachedT{});
+    }
+    __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
+    // the row maxima belong to the VALU phase (the MFMA wave reaches the barrier
+    // as soon as its last products are issued)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xs[0][kb][i]));
+    // ---- V(k): softmax of tile k ----
+    if (KK == kInterior || uses(k)) {
+      softmax_max<1>(xs, m_run, l_run, acc, scale_log2);
+      softmax_exp<1, false>(xs, m_run, l_run, scale_log2, pk);
+    }
+    __syncthreads();
+  };
+
+  int k = 0;
+  for (; k + 1 < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kInterior>{});
+  if (k < n_interior) {
+    if (k + 1 < t_local) tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kEdge>{});
+    else tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kLocal>{});
+    ++k;
+  }
+  {
+    // the base-RoPE query fragment is only needed from the band on
+    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
+  }
+  for (; k < t_local; ++k) {
+    if (k + 1 < t_local) tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kEdge>{});
+    else tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kLocal>{});
+  }
+  for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{}, std::integral_constant<int, kLocal>{});
+  if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lofs, pk, acc);
+  if (grp == 0) __syncthreads();
+
+  // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
+  if (!row_ok) return;
+  const float lt = half_sum(l_run[0]);
+  const float inv = 1.0f / lt;
+  const float lse_v = (m_run[0] * scale_log2 + __builtin_log2f(lt)) * kLn2;
+  uint16_t* o = a.out + ((SEQ_Q0 + my_row) * a.hq + hq) * kD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      u32x2 val = {pack_bf16(acc[0][nb][4 * i4] * inv, acc[0][nb][4 * i4 + 1] * inv),
+                   pack_bf16(acc[0][nb][4 * i4 + 2] * inv, acc[0][nb][4 * i4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(o + 32 * nb + 8 * i4 + 4 * h) = val;
+    }
+  if (a.lse && h == 0) {
+    if constexpr (VARLEN) a.lse[(int64_t)hq * a.total_q + sv.q0 + my_row] = lse_v;
+    else a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = lse_v;
+  }
+}
+
 #undef SEQ_N_Q
 #undef SEQ_POS
 #undef SEQ_N_KV
@@ -1332,7 +1700,14 @@ hipError_t launch_mode(const PrefillProblem& p, hipStream_t stream) {
   }
   if constexpr (MODE == kModePasses)
     hipLaunchKernelGGL((prefill_kernel<MODE, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
-  else if constexpr (MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre) {
+  else if constexpr (MODE == kModeBifocal) {
+    if (p.cu_q)
+      hipLaunchKernelGGL((prefill_fused_kernel<true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    else if (p.q_pos)
+      hipLaunchKernelGGL((prefill_fused_kernel<false, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_fused_kernel<>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+  } else if constexpr (MODE == kModePlain || MODE == kModeBifocalPre) {
     if (p.cu_q)
       hipLaunchKernelGGL((prefill_pp_kernel<MODE, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
     else if (p.q_pos)
