@@ -54,7 +54,7 @@ WORKLOADS = {
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bifocal_fused_qwen3_8b_128k_hbm_traffic.md")
-ROOFLINE_KERNEL = "prefill_pp_kernel<1, false, false>"
+ROOFLINE_KERNEL = "prefill_fused_kernel<false, false>"
 
 
 def measured_traffic():

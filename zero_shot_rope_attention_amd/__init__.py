@@ -45,7 +45,8 @@ __all__ = [
     "jl_qwen3_attention_layer",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
+# JL_LIBRARY may name another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("JL_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjetlong.so")
 
 _i32, _i64, _f32, _f64, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double,
                                     ctypes.c_void_p, ctypes.c_size_t)

@@ -82,8 +82,8 @@ __device__ __forceinline__ SeqSplit seq_split(int s, bool bif, int64_t big_l, in
   r.g = bif ? sched_group(s, big_l, w_req, sched) : 1;
   const int w = min(w_req, s);
   r.remote_end = (r.g > 1 || sliding) ? s - w : 0;
-  r.n_rem = sliding ? 0 : (r.remote_end + kpg - 1) / kpg;
-  r.n_chunks = r.n_rem + (s - r.remote_end + kpg - 1) / kpg;
+  r.n_rem = sliding ? 0 : ceil_div(r.remote_end, kpg);
+  r.n_chunks = r.n_rem + ceil_div(s - r.remote_end, kpg);
   return r;
 }
 
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   bool remote = false;
   int first_local = 0;  // PAGED: keys from here on take base scores
   if constexpr (PAGED) {
-    if (sp >= (s_len + kpg - 1) / kpg) return;  // a shorter sequence of the batch: no chunk here
+    if (sp >= ceil_div(s_len, kpg)) return;  // a shorter sequence of the batch: no chunk here
     ks = sp * kpg;
     ke = min(s_len, ks + kpg);
     first_local = (BIF && sq.g > 1) ? s_len - min(a.local_window, s_len) : 0;
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const C
   const int tid = threadIdx.x;
   const int cl = tid >> 5, c4 = tid & 31;
   const int s_len = seq_length(ca.seq_lens, (int)(bh / ca.hq), ca.n_kv);
-  const int n_wg = ca.paged ? (s_len + ca.kpg - 1) / ca.kpg
+  const int n_wg = ca.paged ? ceil_div(s_len, ca.kpg)
                             : seq_split(s_len, ca.bif != 0, ca.pretrained_window, ca.local_window, ca.kpg,
                                         ca.sliding != 0, ca.sched).n_chunks;
   const float* pl = ca.part_lse + bh * ca.n_wg;  // rows of ca.n_wg slots, the first n_wg filled
@@ -580,7 +580,7 @@ int32_t decode_blocks_per_wave(int32_t batch, int32_t n_kv, int32_t n_kv_heads) 
 
 int32_t decode_max_splits(int32_t batch, int32_t n_kv, int32_t n_kv_heads) {
   const int32_t chunk = kWaves * kBlk * decode_blocks_per_wave(batch, n_kv, n_kv_heads);
-  return (n_kv + chunk - 1) / chunk + 1;
+  return ceil_div(n_kv, chunk) + 1;
 }
 
 size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads) {
@@ -640,25 +640,25 @@ hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t strea
     const int32_t w = p.local_window < p.n_kv ? p.local_window : p.n_kv;
     const int32_t nb_w = decode_blocks_per_wave(p.batch, w, p.n_kv_heads);
     const int32_t chunk_w = kWaves * kBlk * nb_w;
-    if ((w + chunk_w - 1) / chunk_w <= decode_max_splits(p.batch, p.n_kv, p.n_kv_heads)) a.nb = nb_w;
+    if (ceil_div(w, chunk_w) <= decode_max_splits(p.batch, p.n_kv, p.n_kv_heads)) a.nb = nb_w;
   }
   a.kpw = kBlk * a.nb;
   const int32_t chunk = kWaves * a.kpw;
   if (paged) {
     // chunks start at multiples of the chunk: at most ceil(n_kv / chunk) per sequence
-    a.n_wg = (p.n_kv + chunk - 1) / chunk;
+    a.n_wg = ceil_div(p.n_kv, chunk);
   } else if (p.seq_lens) {
     // any length up to n_kv fits (the cut at the local window's start may add one chunk)
     a.n_wg = decode_max_splits(p.batch, p.n_kv, p.n_kv_heads);
   } else if (p.sliding) {
     const int32_t w = p.local_window < p.n_kv ? p.local_window : p.n_kv;
-    a.n_wg = (w + chunk - 1) / chunk;
+    a.n_wg = ceil_div(w, chunk);
   } else {
     // every sequence holds n_kv keys: exactly its chunks (the kernels' cut, on the host)
     const int32_t g = bifocal ? sched_group(p.n_kv, a.pretrained_window, a.local_window, a.sched) : 1;
     const int32_t remote_end = g > 1 ? p.n_kv - (p.local_window < p.n_kv ? p.local_window : p.n_kv) : 0;
-    const int32_t n_rem = (remote_end + chunk - 1) / chunk;
-    a.n_wg = n_rem + (p.n_kv - remote_end + chunk - 1) / chunk;
+    const int32_t n_rem = ceil_div(remote_end, chunk);
+    a.n_wg = n_rem + ceil_div(p.n_kv - remote_end, chunk);
   }
   a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   // theta_d / (2 pi) for this RoPE base, kept per thread for the next call

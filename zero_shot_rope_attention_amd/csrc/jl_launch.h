@@ -27,6 +27,10 @@ enum PrefillMode : int { kModePlain = 0, kModeBifocal = 1, kModePasses = 2, kMod
 enum Schedule : int32_t { kSchedGrouped = 0, kSchedSeam = 1, kSchedFractional = 2 };
 constexpr int32_t kFracGroup = 1 << 30;  // positions must stay below it
 
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (which overflows
+// int32 for a near 2^31).
+__host__ __device__ inline int32_t ceil_div(int32_t a, int32_t b) { return a > 0 ? (a - 1) / b + 1 : 0; }
+
 // Group factor of a sequence of s >= 1 keys (1: the base model, no remote key
 // is moved).  Seam needs w < big_l whenever s > big_l.
 __host__ __device__ inline int32_t sched_group(int32_t s, int64_t big_l, int32_t w, int32_t sched) {

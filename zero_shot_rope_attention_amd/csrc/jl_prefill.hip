@@ -723,10 +723,8 @@ __device__ __forceinline__ void store_k_only(const HalfTile& r, uint8_t* sk, int
   *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c + 8) << 4)) = r.khi;
 }
 
-template <bool kGrouped>
-__device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8_t* skg, uint8_t* sv,
-                                           const f32x2* s_tdelta, const f32x2* base, int j0, int g, float inv_g,
-                                           int half, int gtid) {
+// Registers -> LDS: the group's half of a tile, K (as staged) and V.
+__device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8_t* sv, int half, int gtid) {
   {
     const int row = 32 * half + (gtid >> 4), c = gtid & 15;
     *reinterpret_cast<u32x4*>(sv + row * 256 + (v_chunk(row, c) << 4)) = r.v0;
@@ -735,32 +733,6 @@ __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8
   const int kt = 32 * half + half_tile_key(gtid), c = half_tile_chunk(gtid);
   *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c) << 4)) = r.klo;
   *reinterpret_cast<u32x4*>(sk + kt * 256 + (k_chunk(kt, c + 8) << 4)) = r.khi;
-  if constexpr (kGrouped) {
-    // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g; the
-    // 8 pairs are rotated two at a time to keep few values live.
-    const int u = kt - small_div(j0 % g + kt, g, inv_g);
-    const f32x2* td = s_tdelta + u * kTdStride + 8 * c;
-    const f32x2* bs = base + 8 * c;
-    u32x4 glo, ghi;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      float y1[2], y2[2];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int e = 2 * e2 + q2;
-        const f32x2 cs = cmul(bs[e], td[e]);
-        const float x1 = elem(r.klo, e), x2 = elem(r.khi, e);
-        const f32x2 yr = rot_pair(x1, x2, cs.x, cs.y);
-        y1[q2] = yr.x;
-        y2[q2] = yr.y;
-      }
-      glo[e2] = pack_bf16(y1[0], y1[1]);
-      ghi[e2] = pack_bf16(y2[0], y2[1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    *reinterpret_cast<u32x4*>(skg + kt * 256 + (k_chunk(kt, c) << 4)) = glo;
-    *reinterpret_cast<u32x4*>(skg + kt * 256 + (k_chunk(kt, c + 8) << 4)) = ghi;
-  }
 }
 
 
@@ -833,23 +805,20 @@ struct SeqView {
 
 template <int MODE, bool VARLEN = false, bool QPOS = false>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a) {
-  static_assert(MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre || MODE == kModeSliding,
-                "ping-pong kernel: plain, bifocal or sliding window");
-  static_assert(!(VARLEN || QPOS) || MODE == kModePlain || MODE == kModeBifocal || MODE == kModeBifocalPre,
+  static_assert(MODE == kModePlain || MODE == kModeBifocalPre || MODE == kModeSliding,
+                "ping-pong kernel: plain, bifocal with corrected keys staged, or sliding window "
+                "(the single-kernel bifocal form is prefill_fused_kernel)");
+  static_assert(!(VARLEN || QPOS) || MODE == kModePlain || MODE == kModeBifocalPre,
                 "variable-length batches and explicit positions: plain or bifocal");
   static_assert(!(VARLEN && QPOS), "explicit positions are for uniform batches");
   constexpr bool kSliding = MODE == kModeSliding;   // base scores on the window's keys only
   constexpr bool kGrouped = MODE != kModePlain && !kSliding;  // grouped scores on remote keys
-  constexpr bool kRotate = MODE == kModeBifocal;    // keys corrected here, tile by tile
   constexpr bool kPre = MODE == kModeBifocalPre;    // keys corrected beforehand (a.kg)
   constexpr int kTileBytes = kBN * 256;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];                  // K as cached
   __shared__ __attribute__((aligned(16))) uint8_t s_kg[kGrouped ? 2 * kTileBytes : 16];  // corrected K
   __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];                  // V row-major
-  __shared__ f32x2 s_tdelta[kRotate ? 64 * kTdStride : 1];  // E(-u theta_d), u = 0..63, padded rows
-  __shared__ f32x2 s_base[kRotate ? 4 * kHalfD : 1];     // E(c(j0) theta_d): [group][parity of k]
-  __shared__ double s_theta[kRotate ? kHalfD : 1];       // theta_d / (2 pi) of this sequence
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -948,15 +917,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
   auto k_src = [&](int t) { return (kPre && t < n_interior) ? kgbase : kbase; };
   auto k_dst = [&](int t) { return ((kPre && t < n_interior) ? s_kg : s_k) + (t & 1) * kTileBytes; };
 
-  // rotation table first, while few values are live; theta_d is kept in LDS for
-  // the per-tile base angles (a load from the argument block inside the loop
-  // would put its latency on every tile's VALU phase)
-  if constexpr (kRotate) {
-    if (tid < kHalfD) s_theta[tid] = SEQ_THETA(tid);
-#pragma unroll 1
-    for (int idx = tid; idx < 64 * kHalfD; idx += 512)
-      s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), SEQ_THETA(idx & 63));
-  }
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
   load_half(regs, k_src(t0), vbase, kv_rs, SEQ_N_KV, t0 * kBN, soff);
@@ -997,53 +957,25 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     }
   }
 
-  auto base_angles = [&](int tt, int slot) {  // by the first 64 threads of a group
-    const int j = min(tt, ntiles - 1) * kBN;
-    s_base[slot * kHalfD + (gtid & 63)] = rot_cs((long long)(j / SEQ_G) - j, s_theta[gtid & 63]);
-  };
-  const float inv_g = VARLEN ? 1.0f / (float)sv.g : a.inv_g;
-  auto store = [&](int tt, int slot) {  // slot: rotation-base slot
+  auto store = [&](int tt) {
     if constexpr (kPre) {
-      store_half<false>(regs, k_dst(tt), nullptr, s_v + (tt % 3) * kTileBytes, nullptr, nullptr, 0, 1, 1.0f, grp,
-                        gtid);
+      store_half(regs, k_dst(tt), s_v + (tt % 3) * kTileBytes, grp, gtid);
       if (tt >= n_interior && tt < t_local) {  // edge tile: the corrected keys too
         HalfTile kgr;
         load_k_only(kgr, kgbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
         store_k_only(kgr, s_kg + (tt & 1) * kTileBytes, grp, gtid);
       }
     } else {
-      store_half<kRotate>(regs, s_k + (tt & 1) * kTileBytes, s_kg + (kRotate ? (tt & 1) * kTileBytes : 0),
-                          s_v + (tt % 3) * kTileBytes, s_tdelta, s_base + (kRotate ? slot * kHalfD : 0), tt * kBN,
-                          SEQ_G, inv_g, grp, gtid);
+      store_half(regs, s_k + (tt & 1) * kTileBytes, s_v + (tt % 3) * kTileBytes, grp, gtid);
     }
   };
 
   // ---- prologue: tiles 0 and 1, each group its half ----
-  // s_base slot [grp][k & 1] holds the rotation base of the tile group grp
-  // stages in V(k); the prologue borrows slot [grp][0] for tiles 0 and 1.
-  if constexpr (kRotate) {
-    if (gtid < 64) {
-      s_base[(2 * grp) * kHalfD + gtid] = f32x2{1.0f, 0.0f};  // tile 0: c(0) = 0
-    }
-    __syncthreads();
-  }
-  store(t0, 2 * grp);
+  store(t0);
   __syncthreads();
   if (ntiles > t0 + 1) {
-    if constexpr (kRotate) {
-      if (gtid < 64) base_angles(1, 2 * grp);
-      __syncthreads();
-    }
     load_half(regs, k_src(t0 + 1), vbase, kv_rs, SEQ_N_KV, (t0 + 1) * kBN, soff);
-    store(t0 + 1, 2 * grp);
-  }
-  if constexpr (kRotate) {
-    __syncthreads();
-    // slot [grp][k & 1] holds the base of the tile staged in V(k): the first
-    // in-loop stagings are V(1) (group A, tile 2) and V(0) (group B, tile 2)
-    if (gtid < 64) {
-      base_angles(2, 2 * grp + (grp == 0 ? 1 : 0));
-    }
+    store(t0 + 1);
   }
 
   const LaneOffsets lofs = lane_offsets(lane);
@@ -1087,7 +1019,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // bifocal: they are issued at the start of the VALU phase, so that the 16
     // registers they fill are not live across the MFMA phase, where that kernel
     // has none left
-    if (!kRotate && do_stage) load_half(regs, k_src(tt), vbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
+    if (do_stage) load_half(regs, k_src(tt), vbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (kGrouped ? (k & 1) * kTileBytes : 0);
     // V of tile k-1 (at the first tile the probabilities are zero and that
@@ -1126,24 +1058,18 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xs[0][kb][i]));
     }
-    if (kRotate && do_stage) load_half(regs, kbase, vbase, kv_rs, SEQ_N_KV, tt * kBN, soff);
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || kKind == kLocalFree || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
-      softmax_exp<1, !kRotate>(xs, m_run, l_run, a.scale_log2, pk);
+      softmax_exp<1, true>(xs, m_run, l_run, a.scale_log2, pk);
     }
     // the scores are dead once the probabilities exist: keep the staging after
     __builtin_amdgcn_sched_barrier(0);
     if (do_stage) {
       if constexpr (kKind == kLocal || kKind == kLocalFree)  // every later tile is local: no corrected keys
-        store_half<false>(regs, s_k + (tt & 1) * kTileBytes, nullptr, s_v + (tt % 3) * kTileBytes, nullptr,
-                          nullptr, 0, 1, 1.0f, grp, gtid);
+        store_half(regs, s_k + (tt & 1) * kTileBytes, s_v + (tt % 3) * kTileBytes, grp, gtid);
       else
-        store(tt, 2 * grp + (k & 1));
-    }
-    if constexpr (kRotate && kKind != kLocal && kKind != kLocalFree) {
-      // base of the tile this group stages in V(k+1), into the other slot
-      if (gtid < 64) base_angles(tt + 1, 2 * grp + ((k + 1) & 1));
+        store(tt);
     }
     __syncthreads();
   };
