@@ -192,6 +192,23 @@ jl_status jl_bifocal_decode(const void* q, const void* k_cache, const void* v_ca
                             int64_t local_window, double rope_base, float softmax_scale,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* jl_bifocal_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The chunk partials go to a device array of
+ * 32 MiB that the library holds on each GPU until the process ends (no
+ * hipMalloc, hipFree or other allocating call is made).  Arguments, layouts,
+ * results (bitwise those of jl_bifocal_decode on the same inputs) and errors as
+ * jl_bifocal_decode, plus JL_ERR_UNSUPPORTED when the shape needs more than 32
+ * MiB of workspace (jl_bifocal_decode_workspace_size: batch 8 with 32 query and
+ * 8 KV heads at 128K positions fits, batch 16 does not).  Every call on a GPU uses that GPU's one array:
+ * calls that overlap in time on one GPU (other streams, other host threads) race
+ * and give undefined results; calls in stream order are safe. */
+jl_status jl_bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                    float* lse, int32_t batch, int32_t n_kv, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                    int64_t local_window, double rope_base, float softmax_scale,
+                                    void* stream);
+
 /* Plain decode with the same split-K kernels (no correction, no band). */
 jl_status jl_plain_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
                           float* lse, int32_t batch, int32_t n_kv, int32_t n_q_heads,

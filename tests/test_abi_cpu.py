@@ -467,3 +467,30 @@ def test_paged_decode_validation(lib):
         if not _has_gpu():
             assert call() == DEVICE
     assert bif(sched=1, w=64) == INVALID
+
+
+def test_decode_noalloc_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, batch=1, n_kv=100, hq=4, hkv=2, d=128, big_l=32, w=8,
+                 base=1e4, scale=0.0)
+        a.update(kw)
+        return lib.jl_bifocal_decode_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["batch"], a["n_kv"],
+                                             a["hq"], a["hkv"], a["d"], a["big_l"], a["w"], a["base"], a["scale"],
+                                             None)
+
+    assert call(q=None) == INVALID
+    assert call(out=FAKE + 2) == INVALID
+    assert call(hq=3) == INVALID
+    assert call(w=33) == INVALID
+    assert call(d=64) == UNSUPPORTED
+    assert call(hq=64, hkv=2) == UNSUPPORTED                 # more than 16 query heads per KV head
+    # a shape the 32 MiB device array serves, and one past it: rejected before any
+    # device work, whatever the machine
+    limit = 32 << 20
+    assert lib.jl_bifocal_decode_workspace_size(8, 131072, 32, 8, 128) <= limit
+    assert call(batch=8, n_kv=131072, hq=32, hkv=8, big_l=32768, w=4096, base=1e6) in (DEVICE, OK)
+    assert lib.jl_bifocal_decode_workspace_size(16, 131072, 32, 8, 128) > limit
+    assert call(batch=16, n_kv=131072, hq=32, hkv=8, big_l=32768, w=4096, base=1e6) == UNSUPPORTED
+    assert b"33554432" in lib.jl_last_error()
+    if not _has_gpu():
+        assert call() == DEVICE

@@ -27,6 +27,7 @@ __all__ = [
     "jl_bifocal_decode_workspace_size",
     "jl_bifocal_decode",
     "jl_plain_decode",
+    "jl_bifocal_decode_noalloc",
     "jl_bifocal_decode_varlen",
     "jl_plain_decode_varlen",
     "jl_sliding_prefill",
@@ -67,6 +68,8 @@ _SIGNATURES = {
     "jl_bifocal_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64, _f32,
                                  _vp, _sz, _vp]),
     "jl_plain_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "jl_bifocal_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
+                                         _f32, _vp]),
     "jl_bifocal_decode_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64,
                                         _f32, _vp, _sz, _vp]),
     "jl_plain_decode_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz,
@@ -213,6 +216,16 @@ def jl_plain_decode(q, k_cache, v_cache, out, lse, workspace, softmax_scale=0.0,
     nbytes = workspace.numel() * workspace.element_size()
     _check(load_library().jl_plain_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b, n_kv, hq,
                                           hkv, d, float(softmax_scale), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def jl_bifocal_decode_noalloc(q, k_cache, v_cache, out, lse, pretrained_window, local_window, rope_base,
+                              softmax_scale=0.0, stream=None):
+    """As jl_bifocal_decode, with the library's own device array as the workspace."""
+    b, _, hq, d = q.shape
+    n_kv, hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(load_library().jl_bifocal_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), b,
+                                                    n_kv, hq, hkv, d, int(pretrained_window), int(local_window),
+                                                    float(rope_base), float(softmax_scale), _stream(stream)))
 
 
 def _seq_lens_ptr(seq_lens):

@@ -294,6 +294,39 @@ jl_status jl_bifocal_decode(const void* q, const void* k_cache, const void* v_ca
   return launched(jl::launch_decode(g > 1, p, static_cast<hipStream_t>(stream)));
 }
 
+jl_status jl_bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                    int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int64_t pretrained_window, int64_t local_window,
+                                    double rope_base, float softmax_scale, void* stream) {
+  float scale;
+  const Shape s{batch, 1, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(check_pointer(q, "q"));
+  JL_TRY(check_pointer(k_cache, "k_cache"));
+  JL_TRY(check_pointer(v_cache, "v_cache"));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_shape(s));
+  if (s.hq / s.hkv > 16)
+    return fail(JL_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", s.hq / s.hkv);
+  JL_TRY(check_scale(softmax_scale, &scale));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  const size_t need = jl::decode_workspace_bytes(batch, n_kv, n_q_heads, n_kv_heads);
+  if (need > jl::kDecodeScratchBytes)
+    return fail(JL_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of decode workspace, more than the %zu the allocation-free entry point "
+                "holds; use jl_bifocal_decode with a workspace",
+                need, jl::kDecodeScratchBytes);
+  JL_TRY(device_check());
+  void* ws = nullptr;
+  const hipError_t e = jl::decode_scratch(&ws);
+  if (e != hipSuccess) return fail(JL_ERR_DEVICE, "device workspace address: %s", hipGetErrorString(e));
+  const int64_t g = jl_group_factor(n_kv, pretrained_window);
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  jl::DecodeProblem p{q, k_cache, v_cache, out, lse, nullptr, batch, n_kv, n_q_heads, n_kv_heads, pretrained_window,
+                      w, rope_base, scale, ws};
+  return launched(jl::launch_decode(g > 1, p, static_cast<hipStream_t>(stream)));
+}
+
 jl_status jl_sliding_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
                             int32_t batch, int32_t n_kv, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                             int64_t local_window, float softmax_scale, void* workspace, size_t workspace_bytes,

@@ -588,6 +588,32 @@ size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads, in
   return rows * kD * sizeof(float) + rows * sizeof(float);
 }
 
+// Device-resident workspace of the allocation-free decode entry point: one copy
+// per GPU, kept until the process ends.  Host code uses only the address
+// returned by hipGetSymbolAddress (the array's name is a host-side stand-in).
+// It holds chunk partials only, each written before it is read within a call,
+// so nothing in it has to start at zero; calls that overlap on one GPU share it
+// and race.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];  // per device, filled on first use
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // with device dev current; racing callers get the same address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 // CUs of the current device (queried once per device; 0 if unknown).
 static int device_cu_count() {
   constexpr int kMaxDevices = 64;

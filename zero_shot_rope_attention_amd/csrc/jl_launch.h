@@ -124,6 +124,11 @@ size_t decode_workspace_bytes(int32_t batch, int32_t n_kv, int32_t n_q_heads, in
 
 hipError_t launch_decode(bool bifocal, const DecodeProblem& p, hipStream_t stream);
 
+// The allocation-free decode's workspace: a device array of this many bytes per
+// GPU (its address on the current device in *ptr).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Per-head RMSNorm of the query and key heads, RoPE at the tokens' positions
 // n_kv - n_new + i, and the append of keys and values to the caches.
 struct NormRopeProblem {
