@@ -58,6 +58,15 @@ __device__ __forceinline__ f32x2 rot_cs(long long c, double theta_rev) {
   return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
 }
 
+// rot_cs for a count known to fit 32 bits: the same bits (both conversions to
+// double are exact), one conversion instead of the 64-bit sequence.
+__device__ __forceinline__ f32x2 rot_cs(int c, double theta_rev) {
+  const double cd = (double)c;
+  const double r = cd * theta_rev;
+  const float f = (float)__builtin_fma(cd, theta_rev, -__builtin_rint(r));
+  return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
+}
+
 // acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
 __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u),

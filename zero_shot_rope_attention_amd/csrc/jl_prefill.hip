@@ -738,9 +738,9 @@ __device__ __forceinline__ void store_half(const HalfTile& r, uint8_t* sk, uint8
 
 // Interior MFMA phase: S = K Q^T of tile k (16 MFMAs, two 32-key blocks) and,
 // when kPV, O^T += V^T P^T of tile k-1 (16 MFMAs), issued alternately.  The
-// LDS operands of step i+3 are read while the MFMAs of step i run (a ring of 4
-// operand sets), and the order is pinned so the compiler does not hoist all 48
-// reads ahead of the matrix work.
+// LDS operands of step i + kDist are read while the MFMAs of step i run (a
+// ring of kDist + 1 operand sets), and the order is pinned so the compiler does
+// not hoist all 48 reads ahead of the matrix work.
 // `hook(i)` runs at step i = 0..15 (a constant once unrolled), in the same
 // scheduling region as that step's two MFMAs, so the work it adds issues in
 // the matrix cores' shadow.
@@ -748,11 +748,10 @@ struct NoHook {
   __device__ __forceinline__ void operator()(int) const {}
 };
 
-template <bool kPV, typename Hook = NoHook>
+template <bool kPV, typename Hook = NoHook, int kDist = 2>
 __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8_t* vbuf, const LaneOffsets& lo,
                                                 const bf16x8 (&q)[8], const uint32_t (&pk)[1][2][8],
                                                 f32x16 (&sc)[2], f32x16 (&acc)[1][4], const Hook& hook = Hook()) {
-  constexpr int kDist = 2;
   auto read_k = [&](int i) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(kbuf + lo.k[i >> 1] + (i & 1) * (32 * 256));
   };
@@ -1215,7 +1214,6 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   const int my_p = row_ok ? (QPOS ? SEQ_POS(my_row) : pos_off + my_row) : -1;
   const int w = a.w;
   const int g = SEQ_G;
-  const float inv_g = VARLEN ? 1.0f / (float)sv.g : a.inv_g;
   const float scale_log2 = a.scale_log2;
 
   const int64_t q_rs = (int64_t)a.hq * kD;
@@ -1286,37 +1284,65 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   // this thread: key kt of the tile, rotate-half pairs 8c .. 8c+7
   const int kt = 32 * grp + half_tile_key(gtid);
   const int kc = half_tile_chunk(gtid);
-  // LDS byte offsets of this thread's staging writes, recomputed where they are
-  // used (a few VALU) rather than kept live through the loop
-  auto k_off = [&](int hi) {
+  // LDS byte offsets of this thread's staging writes within a tile, formed
+  // where they are used (a few VALU) rather than kept live through the loop: K
+  // chunks c and c + 8 differ in bit 3 of the swizzled chunk only (offset ^
+  // 128), the V chunk of row + 16 has the same swizzle (offset + 4096); both
+  // offsets are below 2^15 and come packed in one word, K in the low half
+  auto write_offsets = [&]() -> uint32_t {
     int t = gtid;
     asm volatile("" : "+v"(t));
-    const int key = 32 * grp + half_tile_key(t);
-    return key * 256 + (k_chunk(key, half_tile_chunk(t) + 8 * hi) << 4);
+    const int key = 32 * grp + half_tile_key(t), row = 32 * grp + (t >> 4);
+    return (uint32_t)(key * 256 + (k_chunk(key, half_tile_chunk(t)) << 4)) |
+           ((uint32_t)(row * 256 + (v_chunk(row, t & 15) << 4)) << 16);
   };
-  auto v_off = [&](int hi) {
-    int t = gtid;
-    asm volatile("" : "+v"(t));
-    const int row = 32 * grp + (t >> 4) + 16 * hi;
-    return row * 256 + (v_chunk(row, t & 15) << 4);
+  const uint32_t ug = (uint32_t)g;
+  // floor(n / g) for the n = r + kt < g + 64 of the rotation table index: n for
+  // g = 1; the high word of n * ceil(2^32 / g), exact while n g < 2^32 (the
+  // error n (ceil(2^32/g) - 2^32/g) / 2^32 < 1/g stays below the gap of n/g to
+  // the next integer), for 2 <= g <= kMagicMaxG; else n >= g (n < 2g)
+  constexpr uint32_t kMagicMaxG = 65472;  // (g + 64) g < 2^32
+  const int div_mode = g == 1 ? 0 : (ug <= kMagicMaxG ? 1 : 2);
+  const uint32_t g_magic = div_mode == 1 ? (uint32_t)((0x100000000ull + ug - 1) / ug) : 0u;
+  auto floor_div_g = [&](uint32_t n) -> uint32_t {
+    if (div_mode == 0) return n;
+    if (div_mode == 1) return __umulhi(n, g_magic);
+    return n >= ug ? 1u : 0u;
   };
+  // per-tile scalars, advanced once per tile: r = j0 mod g of the tile staged
+  // next (st_r), and of the tile whose loads and rotation base are issued
+  // next (ld_t, its j0 = 64 ld_t, ld_r, ld_q = floor(j0 / g)); ld_t stops at
+  // the last tile (staging past it re-stages the last tile into unread slots)
+  const uint32_t r64 = (uint32_t)kBN % ug, q64 = (uint32_t)kBN / ug;
+  uint32_t st_r = 0;
+  int ld_t = 0;
+  uint32_t ld_r = 0, ld_q = 0;
+  auto advance_ld = [&]() {
+    if (ld_t < ntiles - 1) {
+      ++ld_t;
+      ld_r += r64;
+      ld_q += q64;
+      if (ld_r >= ug) {
+        ld_r -= ug;
+        ++ld_q;
+      }
+    }
+  };
+  int v_slot = 0;  // (tile staged next) mod 3
   const f32x2* td = s_tdelta;
   f32x2 tdr[2], bsr[2];
   float ylo[2], yhi[2];
   u32x4 glo, ghi;
-  const uint32_t ug = (uint32_t)g;  // positions are >= 0: unsigned division, fewer scalar steps
-  auto base_angles = [&](int tt) {  // by the group's first 64 threads
-    const uint32_t j = (uint32_t)(min(tt, ntiles - 1) * kBN);
-    s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rot_cs((long long)(j / ug) - (long long)j, s_theta[gtid]);
+  auto base_angles = [&](int tt) {  // rotation base of tile ld_t, by the group's first 64 threads
+    s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rot_cs((int)ld_q - ld_t * kBN, s_theta[gtid]);
   };
   // kRot: tile tt needs corrected keys; kCached: it needs the keys as cached
   auto stage_step = [&](int tt, int i, auto rot_tag, auto cached_tag) {
     constexpr bool kRot = decltype(rot_tag)::value, kCached = decltype(cached_tag)::value;
-    const int ts = min(tt, ntiles - 1);  // past the last tile: the last one again, into unread slots
     if constexpr (kRot) {
       if (i == 0) {
         // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g
-        const int u = kt - small_div((int)((uint32_t)(ts * kBN) % ug) + kt, g, inv_g);
+        const int u = kt - (int)floor_div_g(st_r + (uint32_t)kt);
         td = s_tdelta + u * kTdStride + 8 * kc;
       }
       const f32x2* bs = s_base + (2 * grp + (tt & 1)) * kHalfD + 8 * kc;
@@ -1335,39 +1361,59 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
         ylo[e & 1] = yr.x;
         yhi[e & 1] = yr.y;
         if (e & 1) {
-          glo[e >> 1] = pack_bf16(ylo[0], ylo[1]);
-          ghi[e >> 1] = pack_bf16(yhi[0], yhi[1]);
+          // pairs e-1 and e came from word e/2 of each half: the corrected pair
+          // replaces it in place unless the keys as cached are stored too
+          u32x4& dlo = kCached ? glo : regs.klo;
+          u32x4& dhi = kCached ? ghi : regs.khi;
+          dlo[e >> 1] = pack_bf16(ylo[0], ylo[1]);
+          dhi[e >> 1] = pack_bf16(yhi[0], yhi[1]);
         }
         if (e + 2 < 8) issue(e + 2);
       }
       if (i == 9) {
+        const uint32_t kw0 = write_offsets() & 0xffffu;
         uint8_t* skg = s_kg + (tt & 1) * kTileBytes;
-        *reinterpret_cast<u32x4*>(skg + k_off(0)) = glo;
-        *reinterpret_cast<u32x4*>(skg + k_off(1)) = ghi;
+        *reinterpret_cast<u32x4*>(skg + kw0) = kCached ? glo : regs.klo;
+        *reinterpret_cast<u32x4*>(skg + (kw0 ^ 128u)) = kCached ? ghi : regs.khi;
       }
     }
     if constexpr (kCached) {
       if (i == 9) {
+        const uint32_t kw0 = write_offsets() & 0xffffu;
         uint8_t* sk = s_k + (tt & 1) * kTileBytes;
-        *reinterpret_cast<u32x4*>(sk + k_off(0)) = regs.klo;
-        *reinterpret_cast<u32x4*>(sk + k_off(1)) = regs.khi;
+        *reinterpret_cast<u32x4*>(sk + kw0) = regs.klo;
+        *reinterpret_cast<u32x4*>(sk + (kw0 ^ 128u)) = regs.khi;
       }
     }
     if (i == 10) {
-      uint8_t* sv = s_v + (tt % 3) * kTileBytes;
-      *reinterpret_cast<u32x4*>(sv + v_off(0)) = regs.v0;
-      *reinterpret_cast<u32x4*>(sv + v_off(1)) = regs.v1;
+      uint8_t* sv = s_v + v_slot * kTileBytes + (write_offsets() >> 16);
+      *reinterpret_cast<u32x4*>(sv) = regs.v0;
+      *reinterpret_cast<u32x4*>(sv + 16 * 256) = regs.v1;
     }
-    if (i == 11) load_half(regs, kbase, vbase, kv_rs, n_kv, min(tt + 1, ntiles - 1) * kBN, soff);
-    if (i == 12 && gtid < 64) base_angles(tt + 1);
+    if (i == 15) {
+      // last, after any reload of the phase (a reload issued after these loads
+      // would wait for them); the lane's load offsets are formed here rather
+      // than kept live through the loop
+      int t = gtid;
+      asm volatile("" : "+v"(t));
+      load_half(regs, kbase, vbase, kv_rs, n_kv, ld_t * kBN, stage_offsets(kv_rs, grp, t));
+    }
+    if (i == 11 && gtid < 64) base_angles(tt + 1);
   };
-  constexpr int kStageSteps = 13;
+  // after the staging of a tile: the next one's scalars
+  auto next_stage = [&]() {
+    st_r = ld_r;
+    advance_ld();
+    v_slot = v_slot == 2 ? 0 : v_slot + 1;
+  };
+  constexpr int kStageSteps = 16;
   using TT = std::true_type;
   using FF = std::false_type;
 
   // ---- prologue: tile 0 staged, the loads and rotation base of tile 1 issued ----
   __syncthreads();  // theta table
   if (gtid < 64) base_angles(0);
+  advance_ld();  // the prologue's loads and rotation base are tile 1's
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kStageSteps; ++i) {
@@ -1375,6 +1421,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     else if (t_local > 0) stage_step(0, i, TT{}, TT{});
     else stage_step(0, i, FF{}, TT{});
   }
+  next_stage();
 
   const LaneOffsets lofs = lane_offsets(lane);
   float m_run[1] = {kNegBig}, l_run[1] = {0.0f};
@@ -1408,7 +1455,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       auto hook = [&](int i) {
         if (i < kStageSteps) stage_step(k + 1, i, RotT{}, CachedT{});
       };
-      mphase_interior<true>(skg, svp, lofs, qg, pk, sc, acc, hook);
+      // operands read one step ahead: the staging work makes a step long enough
+      // to cover the LDS latency, and the two registers sets saved are needed
+      mphase_interior<true, decltype(hook), 1>(skg, svp, lofs, qg, pk, sc, acc, hook);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1441,6 +1490,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       softmax_max<1>(xs, m_run, l_run, acc, scale_log2);
       softmax_exp<1, false>(xs, m_run, l_run, scale_log2, pk);
     }
+    next_stage();
     __syncthreads();
   };
 
