@@ -19,6 +19,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -58,12 +59,18 @@ __device__ __forceinline__ f32x2 rot_cs(long long c, double theta_rev) {
   return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
 }
 
-// rot_cs for a count known to fit 32 bits: the same bits (both conversions to
-// double are exact), one conversion instead of the 64-bit sequence.
-__device__ __forceinline__ f32x2 rot_cs(int c, double theta_rev) {
+// The reduced angle of rot_cs alone, c theta_d in [-1/2, 1/2] revolutions, for
+// a count known to fit 32 bits (both conversions to double are exact).
+__device__ __forceinline__ float rev_reduce(int c, double theta_rev) {
   const double cd = (double)c;
   const double r = cd * theta_rev;
-  const float f = (float)__builtin_fma(cd, theta_rev, -__builtin_rint(r));
+  return (float)__builtin_fma(cd, theta_rev, -__builtin_rint(r));
+}
+
+// rot_cs for a count known to fit 32 bits: the same bits, one conversion
+// instead of the 64-bit sequence.
+__device__ __forceinline__ f32x2 rot_cs(int c, double theta_rev) {
+  const float f = rev_reduce(c, theta_rev);
   return f32x2{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
 }
 

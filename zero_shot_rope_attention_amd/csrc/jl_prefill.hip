@@ -82,10 +82,10 @@ __device__ __forceinline__ int k_chunk(int row, int chunk) {
 // PV operand (4 keys x 64 bytes per half-wave) hit all 64 LDS banks once.
 __device__ __forceinline__ int v_chunk(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
-// Rows of the small-angle rotation table E(-u theta_d) are padded by 16 bytes,
-// so that threads staging different keys (different u) with the same d
-// columns fall on different LDS banks.
-constexpr int kTdStride = kHalfD + 2;
+// Rows of the single kernel's small-angle table (-u theta_d in revolutions)
+// are padded by 16 bytes, so that the 16 lanes of a 16-byte read (two keys,
+// eight chunks) fall on different banks when their u differ by one.
+constexpr int kUangStride = kHalfD + 4;
 
 // Key (within a 32-key block) that MFMA row m of S^T stands for.  With this
 // permutation, lane half h holds keys 16h .. 16h+15 of the block in output
@@ -117,6 +117,26 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   const int dcol = 16 * ((lane >> 4) & 1) + 4 * (j & 3);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) o.v[nb] = key * 256 + (v_chunk(key, (32 * nb + dcol) >> 3) << 4) + ((dcol & 7) << 1);
+  return o;
+}
+
+// The same offsets from two words: the swizzles only flip address bits 5-7 (K:
+// fragment kk is fragment 0 with kk in bits 5-7) and 6-7 (V: column block nb
+// is block 0 with nb in bits 6-7), and tile buffers are 16 KB aligned, so the
+// flips commute with adding a buffer's base.
+struct LaneBase {
+  uint32_t k0, v0;
+};
+__device__ __forceinline__ LaneBase lane_base(int lane) {
+  const LaneOffsets o = lane_offsets(lane);
+  return LaneBase{(uint32_t)o.k[0], (uint32_t)o.v[0]};
+}
+__device__ __forceinline__ LaneOffsets lane_expand(const LaneBase& b) {
+  LaneOffsets o;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) o.k[kk] = (int)(b.k0 ^ ((uint32_t)kk << 5));
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) o.v[nb] = (int)(b.v0 ^ ((uint32_t)nb << 6));
   return o;
 }
 
@@ -795,6 +815,54 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
   sc[1] = s1;
 }
 
+// mphase_interior for the single-kernel bifocal prefill: operands read one
+// step ahead and addressed from the lane's two base offsets (LaneBase), which
+// keeps ten registers free for the staging work the hook adds.
+template <typename Hook>
+__device__ __forceinline__ void mphase_compact(const uint8_t* kbuf, const uint8_t* vbuf, const LaneBase& lb,
+                                               const bf16x8 (&q)[8], const uint32_t (&pk)[1][2][8],
+                                               f32x16 (&sc)[2], f32x16 (&acc)[1][4], const Hook& hook) {
+  const uint32_t kb = (uint32_t)(uintptr_t)lds_ptr(kbuf) + lb.k0;
+  auto read_k = [&](int i) -> u32x4 {
+    const lds_byte* p = (const lds_byte*)(uintptr_t)(kb ^ ((uint32_t)(i >> 1) << 5));
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p + (i & 1) * (32 * 256));
+  };
+  const uint32_t vb = (uint32_t)(uintptr_t)lds_ptr(vbuf) + lb.v0;
+  const lds_byte* vp[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) vp[nb] = lds_opaque((const lds_byte*)(uintptr_t)(vb ^ ((uint32_t)nb << 6)));
+  auto read_v = [&](int i) -> u32x4 {
+    const int st = i >> 2, nb = i & 3;
+    const int kbk = st >> 1, half = st & 1;
+    const u32x2 t0 = lds_read_tr16(vp[nb] + (32 * kbk + 8 * half) * 256);
+    const u32x2 t1 = lds_read_tr16(vp[nb] + (32 * kbk + 8 * half + 4) * 256);
+    return u32x4{t0.x, t0.y, t1.x, t1.y};
+  };
+  u32x4 kr[2], vr[2];
+  kr[0] = read_k(0);
+  vr[0] = read_v(0);
+  f32x16 s0 = {}, s1 = {};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + 1 < 16) {
+      kr[(i + 1) & 1] = read_k(i + 1);
+      vr[(i + 1) & 1] = read_v(i + 1);
+    }
+    const bf16x8 ka = as_bf16x8(kr[i & 1]);
+    if (i & 1) s1 = mfma32(ka, q[i >> 1], s1);
+    else s0 = mfma32(ka, q[i >> 1], s0);
+    const int st = i >> 2, nb = i & 3;
+    const int kbk = st >> 1, half = st & 1;
+    const u32x4 pf = {pk[0][kbk][4 * half], pk[0][kbk][4 * half + 1], pk[0][kbk][4 * half + 2],
+                      pk[0][kbk][4 * half + 3]};
+    acc[0][nb] = mfma32(as_bf16x8(vr[i & 1]), as_bf16x8(pf), acc[0][nb]);
+    hook(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sc[0] = s0;
+  sc[1] = s1;
+}
+
 // One sequence of a variable-length batch, as the prefill kernel sees it.
 struct SeqView {
   int n_q, n_kv, n_qblocks, g, q_shift;
@@ -1131,34 +1199,44 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 // The ping-pong of prefill_pp_kernel (waves 0-3 and 4-7 half a tile apart, one
 // group in its MFMA phase while the other is in its VALU phase), with the
 // staging of the next key tile moved into the MFMA phase: the correction
-// rotation of its keys, its LDS writes, the loads of the tile after it and that
-// tile's rotation base are spread over the steps of the MFMA sequence, and the
-// VALU phase keeps the softmax only.  A wave issues about one instruction per
-// 4-5 cycles whatever its kind, so a VALU phase holding both the softmax and
-// the rotation outlasts the other group's MFMA phase, whose wave leaves most of
-// its own issue slots idle between MFMAs.
+// rotation of its keys, its LDS writes and the loads of the tile after it are
+// spread over the steps of the MFMA sequence.  A wave issues about one
+// instruction per 4-5 cycles whatever its kind, so a VALU phase holding both
+// the softmax and the rotation outlasts the other group's MFMA phase, whose
+// wave leaves most of its own issue slots idle between MFMAs.  What the
+// rotation needs first (the tile's rotation base and each thread's row of the
+// small-angle table) is prepared in the VALU phase before, which has slack.
+//
+// A key's angle c(j) theta_d = c(j0) theta_d - u theta_d, u = j - j0 - (floor(j
+// / g) - floor(j0 / g)) < 64: the tile's base angle (exact integer c(j0), fp64
+// reduction, one wave per group per tile) plus a small-angle table entry, both
+// in revolutions, then the hardware cosine and sine.
 //
 // Tile program of each group for tile k:
 //   M(k): S = K^g Q^T of tile k and O^T += V^T P^T of tile k-1 (MFMA), and the
 //         group's half of tile k+1 into LDS (corrected keys, the keys as cached
-//         for band tiles, values), then the loads of its half of tile k+2 and
-//         that tile's rotation base.
-//   V(k): the softmax of tile k.
+//         for band tiles, values), then the loads of its half of tile k+2.
+//   V(k): the softmax of tile k, then tile k+2's rotation base and each
+//         thread's small-angle row for it.
 // Tile k+1 is written in M(k) by both groups, into the K / K^g buffer of tile
 // k-1 and the V buffer of tile k-2, all last read in M(k-1) of both groups;
 // rotation bases sit in two slots per group (tile & 1): tile k+2's is written
-// at the end of M(k), after the staging of tile k+1 has read its own.  Staging past the last tile re-stages the
-// last one into slots no later phase reads, so the loop has no branches.
+// in V(k), the slot of tile k, whose staging in M(k-1) read it last.  Staging
+// past the last tile re-stages the last one into slots no later phase reads,
+// so the loop has no branches.
 // ---------------------------------------------------------------------------
 template <bool VARLEN = false, bool QPOS = false>
 __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs a) {
   static_assert(!(VARLEN && QPOS), "explicit positions are for uniform batches");
   constexpr int kTileBytes = kBN * 256;
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kTileBytes];     // K as cached (band tiles)
-  __shared__ __attribute__((aligned(16))) uint8_t s_kg[2 * kTileBytes];    // corrected K
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[3 * kTileBytes];     // V row-major
-  __shared__ __attribute__((aligned(16))) f32x2 s_tdelta[64 * kTdStride];  // E(-u theta_d), u < 64
-  __shared__ __attribute__((aligned(16))) f32x2 s_base[4 * kHalfD];        // E(c(j0) theta_d): [group][tile & 1]
+  // tile buffers, 16 KB aligned (LaneBase): K as cached (band tiles) x 2,
+  // corrected K x 2, V row-major x 3
+  __shared__ __attribute__((aligned(16384))) uint8_t s_tiles[7 * kTileBytes];
+  uint8_t* const s_k = s_tiles;
+  uint8_t* const s_kg = s_tiles + 2 * kTileBytes;
+  uint8_t* const s_v = s_tiles + 4 * kTileBytes;
+  __shared__ __attribute__((aligned(16))) float s_uang[64 * kUangStride];  // -u theta_d in revolutions, u < 64
+  __shared__ __attribute__((aligned(16))) float s_base[4 * kHalfD];        // c(j0) theta_d, revolutions: [group][tile & 1]
   __shared__ double s_theta[kHalfD];                                        // theta_d / (2 pi)
 
   const int tid = threadIdx.x;
@@ -1238,7 +1316,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   if (tid < kHalfD) s_theta[tid] = SEQ_THETA(tid);
 #pragma unroll 1
   for (int idx = tid; idx < 64 * kHalfD; idx += 512)
-    s_tdelta[(idx >> 6) * kTdStride + (idx & 63)] = rot_cs(-(long long)(idx >> 6), SEQ_THETA(idx & 63));
+    s_uang[(idx >> 6) * kUangStride + (idx & 63)] = rev_reduce(-(idx >> 6), SEQ_THETA(idx & 63));
 
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
@@ -1277,12 +1355,11 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     }
   }
 
-  // ---- staging of this group's half of tile tt: 13 steps, run one per MFMA
-  // step of an interior tile's MFMA phase, or back to back otherwise: the
-  // corrected keys, the LDS writes, then the loads of the next tile and its
-  // rotation base ----
-  // this thread: key kt of the tile, rotate-half pairs 8c .. 8c+7
-  const int kt = 32 * grp + half_tile_key(gtid);
+  // ---- staging of this group's half of tile tt: 16 steps, run one per MFMA
+  // step of an interior tile's MFMA phase, or back to back otherwise: the angle
+  // terms (step 0), the corrected keys (steps 3-10), the LDS writes (11, 12),
+  // then the loads of the next tile (15) ----
+  // this thread: key kt = 32 grp + gtid / 8 of the tile, rotate-half pairs 8c .. 8c+7
   const int kc = half_tile_chunk(gtid);
   // LDS byte offsets of this thread's staging writes within a tile, formed
   // where they are used (a few VALU) rather than kept live through the loop: K
@@ -1297,24 +1374,23 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
            ((uint32_t)(row * 256 + (v_chunk(row, t & 15) << 4)) << 16);
   };
   const uint32_t ug = (uint32_t)g;
-  // floor(n / g) for the n = r + kt < g + 64 of the rotation table index: n for
-  // g = 1; the high word of n * ceil(2^32 / g), exact while n g < 2^32 (the
-  // error n (ceil(2^32/g) - 2^32/g) / 2^32 < 1/g stays below the gap of n/g to
-  // the next integer), for 2 <= g <= kMagicMaxG; else n >= g (n < 2g)
-  constexpr uint32_t kMagicMaxG = 65472;  // (g + 64) g < 2^32
-  const int div_mode = g == 1 ? 0 : (ug <= kMagicMaxG ? 1 : 2);
-  const uint32_t g_magic = div_mode == 1 ? (uint32_t)((0x100000000ull + ug - 1) / ug) : 0u;
+  // floor(n / g) for the n = r + kt < g + 64 of the rotation table index,
+  // without a division or a branch: the high word of n * ceil(2^32 / g), exact
+  // while n g < 2^32 (the error n (ceil(2^32/g) - 2^32/g) / 2^32 < 1/g stays
+  // below the gap of n/g to the next integer), for 2 <= g <= kMagicMaxG; n for
+  // g = 1 (magic 0, n added once); (n >= g) above (magic 0, n < 2g)
+  constexpr uint32_t kMagicMaxG = 65472;  // (g + 63) g < 2^32
+  const uint32_t g_magic = (g > 1 && ug <= kMagicMaxG) ? (uint32_t)((0x100000000ull + ug - 1) / ug) : 0u;
+  const uint32_t g_one = g == 1 ? 1u : 0u;
+  const uint32_t g_cmp = ug > kMagicMaxG ? ug : 0xffffffffu;
   auto floor_div_g = [&](uint32_t n) -> uint32_t {
-    if (div_mode == 0) return n;
-    if (div_mode == 1) return __umulhi(n, g_magic);
-    return n >= ug ? 1u : 0u;
+    return __umulhi(n, g_magic) + n * g_one + (n >= g_cmp ? 1u : 0u);
   };
-  // per-tile scalars, advanced once per tile: r = j0 mod g of the tile staged
-  // next (st_r), and of the tile whose loads and rotation base are issued
-  // next (ld_t, its j0 = 64 ld_t, ld_r, ld_q = floor(j0 / g)); ld_t stops at
-  // the last tile (staging past it re-stages the last tile into unread slots)
+  // per-tile scalars, advanced once per tile: the tile whose loads, rotation
+  // base and angle rows are prepared next (ld_t, its j0 = 64 ld_t, ld_r = j0
+  // mod g, ld_q = floor(j0 / g)); ld_t stops at the last tile (staging past it
+  // re-stages the last tile into unread slots)
   const uint32_t r64 = (uint32_t)kBN % ug, q64 = (uint32_t)kBN / ug;
-  uint32_t st_r = 0;
   int ld_t = 0;
   uint32_t ld_r = 0, ld_q = 0;
   auto advance_ld = [&]() {
@@ -1329,34 +1405,30 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     }
   };
   int v_slot = 0;  // (tile staged next) mod 3
-  const f32x2* td = s_tdelta;
-  f32x2 tdr[2], bsr[2];
+  int ua_off = 0;       // this thread's small-angle row for the tile staged next (entries)
+  f32x4 uar[2], bsr[2];  // the angle terms of pairs 4b .. 4b+3 (block b)
   float ylo[2], yhi[2];
   u32x4 glo, ghi;
   auto base_angles = [&](int tt) {  // rotation base of tile ld_t, by the group's first 64 threads
-    s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rot_cs((int)ld_q - ld_t * kBN, s_theta[gtid]);
+    s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rev_reduce((int)ld_q - ld_t * kBN, s_theta[gtid]);
   };
   // kRot: tile tt needs corrected keys; kCached: it needs the keys as cached
   auto stage_step = [&](int tt, int i, auto rot_tag, auto cached_tag) {
     constexpr bool kRot = decltype(rot_tag)::value, kCached = decltype(cached_tag)::value;
     if constexpr (kRot) {
-      if (i == 0) {
-        // c(j) = c(j0) - u with u = kt - floor((r + kt) / g), r = j0 mod g
-        const int u = kt - (int)floor_div_g(st_r + (uint32_t)kt);
-        td = s_tdelta + u * kTdStride + 8 * kc;
+      if (i == 0) {  // the angle terms of all 8 pairs: 16-byte reads, two per table
+        const float* ua = s_uang + ua_off;
+        const float* bs = s_base + (2 * grp + (tt & 1)) * kHalfD + 8 * kc;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          uar[b] = *reinterpret_cast<const f32x4*>(ua + 4 * b);
+          bsr[b] = *reinterpret_cast<const f32x4*>(bs + 4 * b);
+        }
       }
-      const f32x2* bs = s_base + (2 * grp + (tt & 1)) * kHalfD + 8 * kc;
-      auto issue = [&](int e) {
-        tdr[e & 1] = td[e];
-        bsr[e & 1] = bs[e];
-      };
-      if (i == 0) {
-        issue(0);
-        issue(1);
-      }
-      if (i >= 1 && i <= 8) {  // pair e = i - 1; the reads of pair e + 2 follow it
-        const int e = i - 1;
-        const f32x2 cs = cmul(bsr[e & 1], tdr[e & 1]);
+      if (i >= 3 && i <= 10) {  // pair e = i - 3 (three steps after the reads): c(j0) theta_d - u theta_d
+        const int e = i - 3;
+        const float ang = bsr[e >> 2][e & 3] + uar[e >> 2][e & 3];
+        const f32x2 cs = {__builtin_amdgcn_cosf(ang), __builtin_amdgcn_sinf(ang)};
         const f32x2 yr = rot_pair(elem(regs.klo, e), elem(regs.khi, e), cs.x, cs.y);
         ylo[e & 1] = yr.x;
         yhi[e & 1] = yr.y;
@@ -1368,9 +1440,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
           dlo[e >> 1] = pack_bf16(ylo[0], ylo[1]);
           dhi[e >> 1] = pack_bf16(yhi[0], yhi[1]);
         }
-        if (e + 2 < 8) issue(e + 2);
       }
-      if (i == 9) {
+      if (i == 11) {
         const uint32_t kw0 = write_offsets() & 0xffffu;
         uint8_t* skg = s_kg + (tt & 1) * kTileBytes;
         *reinterpret_cast<u32x4*>(skg + kw0) = kCached ? glo : regs.klo;
@@ -1378,14 +1449,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       }
     }
     if constexpr (kCached) {
-      if (i == 9) {
+      if (i == 11) {
         const uint32_t kw0 = write_offsets() & 0xffffu;
         uint8_t* sk = s_k + (tt & 1) * kTileBytes;
         *reinterpret_cast<u32x4*>(sk + kw0) = regs.klo;
         *reinterpret_cast<u32x4*>(sk + (kw0 ^ 128u)) = regs.khi;
       }
     }
-    if (i == 10) {
+    if (i == 12) {
       uint8_t* sv = s_v + v_slot * kTileBytes + (write_offsets() >> 16);
       *reinterpret_cast<u32x4*>(sv) = regs.v0;
       *reinterpret_cast<u32x4*>(sv + 16 * 256) = regs.v1;
@@ -1398,11 +1469,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       asm volatile("" : "+v"(t));
       load_half(regs, kbase, vbase, kv_rs, n_kv, ld_t * kBN, stage_offsets(kv_rs, grp, t));
     }
-    if (i == 11 && gtid < 64) base_angles(tt + 1);
+  };
+  // this thread's small-angle row for a tile whose j0 mod g is r: c(j) =
+  // c(j0) - u with u = kt - floor((r + kt) / g)
+  auto angle_row = [&](uint32_t r) {
+    int t = gtid;  // kt formed here rather than kept live
+    asm volatile("" : "+v"(t));
+    const int key = 32 * grp + half_tile_key(t);
+    const int u = key - (int)floor_div_g(r + (uint32_t)key);
+    ua_off = u * kUangStride + 8 * kc;
   };
   // after the staging of a tile: the next one's scalars
   auto next_stage = [&]() {
-    st_r = ld_r;
     advance_ld();
     v_slot = v_slot == 2 ? 0 : v_slot + 1;
   };
@@ -1410,20 +1488,24 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   using TT = std::true_type;
   using FF = std::false_type;
 
-  // ---- prologue: tile 0 staged, the loads and rotation base of tile 1 issued ----
+  // ---- prologue: tile 0 staged, the loads, rotation base and angle row of
+  // tile 1 ----
   __syncthreads();  // theta table
   if (gtid < 64) base_angles(0);
   advance_ld();  // the prologue's loads and rotation base are tile 1's
   __syncthreads();
+  angle_row(0u);
 #pragma unroll
   for (int i = 0; i < kStageSteps; ++i) {
     if (n_interior > 0) stage_step(0, i, TT{}, FF{});
     else if (t_local > 0) stage_step(0, i, TT{}, TT{});
     else stage_step(0, i, FF{}, TT{});
   }
+  if (gtid < 64) base_angles(1);
+  angle_row(ld_r);
   next_stage();
 
-  const LaneOffsets lofs = lane_offsets(lane);
+  const LaneBase lbase = lane_base(lane);
   float m_run[1] = {kNegBig}, l_run[1] = {0.0f};
   f32x16 acc[1][4];
 #pragma unroll
@@ -1448,8 +1530,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     __builtin_amdgcn_s_setprio(2);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (k & 1) * kTileBytes;
-    // V of tile k-1 (at tile 0 the probabilities are zero and tile 0's finite V is read)
-    const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) % 3) * kTileBytes;
+    // V of tile k-1, slot (k - 1) mod 3 = (v_slot + 1) mod 3 (at tile 0 the
+    // probabilities are zero and tile 0's finite V is read)
+    const uint8_t* svp = s_v + (k > 0 ? (v_slot == 2 ? 0 : v_slot + 1) : 0) * kTileBytes;
     if constexpr (KK == kInterior) {
       f32x16 sc[2];
       auto hook = [&](int i) {
@@ -1457,7 +1540,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       };
       // operands read one step ahead: the staging work makes a step long enough
       // to cover the LDS latency, and the two registers sets saved are needed
-      mphase_interior<true, decltype(hook), 1>(skg, svp, lofs, qg, pk, sc, acc, hook);
+      mphase_compact(skg, svp, lbase, qg, pk, sc, acc, hook);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1468,12 +1551,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
         if constexpr (KK == kEdge) {
           const bool use_grp = j0 <= wp_hi - w;
           const bool use_base = j0 + kBN - 1 >= wp_lo - w + 1;
-          tile_scores<kModeBifocal, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, w, use_base, use_grp, xs);
+          tile_scores<kModeBifocal, false, 1>(sk, skg, lane_expand(lbase), qf, qg, lane, j0, my_p, w, use_base,
+                                              use_grp, xs);
         } else {
-          tile_scores<kModePlain, false, 1>(sk, skg, lofs, qf, qg, lane, j0, my_p, w, true, false, xs);
+          tile_scores<kModePlain, false, 1>(sk, skg, lane_expand(lbase), qf, qg, lane, j0, my_p, w, true, false,
+                                            xs);
         }
       }
-      if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lofs, pk, acc);
+      if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lane_expand(lbase), pk, acc);
 #pragma unroll
       for (int i = 0; i < kStageSteps; ++i) stage_step(k + 1, i, RotT{}, CachedT{});
     }
@@ -1490,6 +1575,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       softmax_max<1>(xs, m_run, l_run, acc, scale_log2);
       softmax_exp<1, false>(xs, m_run, l_run, scale_log2, pk);
     }
+    // for tile k+2, staged in the next MFMA phase: its rotation base (slot
+    // (k+2) & 1, last read when tile k was staged), by the group's first wave,
+    // and each thread's small-angle row (its r is ld_r).  This phase has slack;
+    // in the MFMA phase that one wave's extra work and the row's dependent reads
+    // held back the barrier
+    if (gtid < 64) base_angles(k + 2);
+    angle_row(ld_r);
     next_stage();
     __syncthreads();
   };
@@ -1513,7 +1605,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     else tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kLocal>{});
   }
   for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{}, std::integral_constant<int, kLocal>{});
-  if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lofs, pk, acc);
+  if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lane_expand(lbase), pk, acc);
   if (grp == 0) __syncthreads();
 
   // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
