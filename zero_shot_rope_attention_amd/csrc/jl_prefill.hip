@@ -815,6 +815,17 @@ __device__ __forceinline__ void mphase_interior(const uint8_t* kbuf, const uint8
   sc[1] = s1;
 }
 
+// A workgroup barrier that orders this wave's LDS reads and writes (lgkmcnt)
+// but not its direct V copies still in flight, which __syncthreads would wait
+// for; the "memory" clobber keeps the compiler from moving memory accesses
+// across it.  Each V copy is waited for by its own wave (the key loads issued
+// after it) before the barrier that ends the next MFMA phase, two phases
+// before the tile is first read.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt not waited for
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // mphase_interior for the single-kernel bifocal prefill: operands read one
 // step ahead and addressed from the lane's two base offsets (LaneBase), which
 // keeps ten registers free for the staging work the hook adds.
@@ -1214,27 +1225,34 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 //
 // Tile program of each group for tile k:
 //   M(k): S = K^g Q^T of tile k and O^T += V^T P^T of tile k-1 (MFMA), and the
-//         group's half of tile k+1 into LDS (corrected keys, the keys as cached
-//         for band tiles, values), then the loads of its half of tile k+2.
+//         group's half of tile k+1's keys into LDS (corrected, and as cached
+//         for band tiles), then its half of tile k+2: the V rows copied
+//         straight from memory into LDS, the keys loaded into registers.
 //   V(k): the softmax of tile k, then tile k+2's rotation base and each
 //         thread's small-angle row for it.
-// Tile k+1 is written in M(k) by both groups, into the K / K^g buffer of tile
-// k-1 and the V buffer of tile k-2, all last read in M(k-1) of both groups;
-// rotation bases sit in two slots per group (tile & 1): tile k+2's is written
-// in V(k), the slot of tile k, whose staging in M(k-1) read it last.  Staging
-// past the last tile re-stages the last one into slots no later phase reads,
-// so the loop has no branches.
+// Tile k+1's keys are written in M(k) by both groups into the K / K^g buffers
+// of tile k-1, last read in M(k-1) of both groups.  V rows sit in four slots
+// (tile & 3): tile k+2's copies land in the slot of tile k-2, last read in
+// M(k-1), and are complete (each wave waits for them with its key loads in
+// M(k+1)) two phases before M(k+3) first reads them; the loop's barriers wait
+// for LDS operations only, so the copies stay in flight across them.  Rotation
+// bases sit in two slots per group (tile & 1): tile k+2's is written in V(k),
+// the slot of tile k, whose staging in M(k-1) read it last.  Staging past the
+// last tile re-stages the last one into slots no later phase reads, so the
+// loop has no branches.
 // ---------------------------------------------------------------------------
 template <bool VARLEN = false, bool QPOS = false>
 __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs a) {
   static_assert(!(VARLEN && QPOS), "explicit positions are for uniform batches");
   constexpr int kTileBytes = kBN * 256;
-  // tile buffers, 16 KB aligned (LaneBase): K as cached (band tiles) x 2,
-  // corrected K x 2, V row-major x 3
-  __shared__ __attribute__((aligned(16384))) uint8_t s_tiles[7 * kTileBytes];
+  // tile buffers, 16 KB aligned (LaneBase): K as cached (band tiles) x 2 and
+  // corrected K x 2; V row-major x 4 (tile t in slot t & 3), an object of its
+  // own, so that the compiler waits for the copies into it only before V reads
+  __shared__ __attribute__((aligned(16384))) uint8_t s_tiles[4 * kTileBytes];
+  __shared__ __attribute__((aligned(16384))) uint8_t s_vt[4 * kTileBytes];
   uint8_t* const s_k = s_tiles;
   uint8_t* const s_kg = s_tiles + 2 * kTileBytes;
-  uint8_t* const s_v = s_tiles + 4 * kTileBytes;
+  uint8_t* const s_v = s_vt;
   __shared__ __attribute__((aligned(16))) float s_uang[64 * kUangStride];  // -u theta_d in revolutions, u < 64
   __shared__ __attribute__((aligned(16))) float s_base[4 * kHalfD];        // c(j0) theta_d, revolutions: [group][tile & 1]
   __shared__ double s_theta[kHalfD];                                        // theta_d / (2 pi)
@@ -1318,9 +1336,27 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   for (int idx = tid; idx < 64 * kHalfD; idx += 512)
     s_uang[(idx >> 6) * kUangStride + (idx & 63)] = rev_reduce(-(idx >> 6), SEQ_THETA(idx & 63));
 
+  // V rows go from memory straight into their LDS slot: this wave's 8 rows of
+  // the group's half of a tile, two 16-byte copies per lane (lane l: row 4r +
+  // l / 16, LDS position l % 16, so it fetches chunk v_chunk(row, l % 16))
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto copy_v = [&](int tt, int j0) {
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, kv_rs, n_kv, j0);
+    int t = lane;  // offsets formed here rather than kept live
+    asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 32 * grp + 8 * (wave & 3) + 4 * r + (t >> 4);
+      const uint32_t vo = (uint32_t)row * (uint32_t)(kv_rs * 2) + 16u * (uint32_t)v_chunk(row, t & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (lds_void*)(s_v + (tt & 3) * kTileBytes + (32 * grp + 8 * (wave & 3) + 4 * r) * 256), 16, (int)vo,
+          0, 0, 0);
+    }
+  };
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
-  load_half(regs, kbase, vbase, kv_rs, n_kv, 0, soff);
+  copy_v(0, 0);
+  load_k_only(regs, kbase, kv_rs, n_kv, 0, soff);
 
   bf16x8 qf[8];
   bf16x8 qg[8];
@@ -1357,22 +1393,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
 
   // ---- staging of this group's half of tile tt: 16 steps, run one per MFMA
   // step of an interior tile's MFMA phase, or back to back otherwise: the angle
-  // terms (step 0), the corrected keys (steps 3-10), the LDS writes (11, 12),
-  // then the loads of the next tile (15) ----
+  // terms (step 0), the corrected keys (steps 3-10), their LDS writes (11),
+  // then the next tile's V copies and key loads (15) ----
   // this thread: key kt = 32 grp + gtid / 8 of the tile, rotate-half pairs 8c .. 8c+7
   const int kc = half_tile_chunk(gtid);
-  // LDS byte offsets of this thread's staging writes within a tile, formed
-  // where they are used (a few VALU) rather than kept live through the loop: K
-  // chunks c and c + 8 differ in bit 3 of the swizzled chunk only (offset ^
-  // 128), the V chunk of row + 16 has the same swizzle (offset + 4096); both
-  // offsets are below 2^15 and come packed in one word, K in the low half
-  auto write_offsets = [&]() -> uint32_t {
-    int t = gtid;
-    asm volatile("" : "+v"(t));
-    const int key = 32 * grp + half_tile_key(t), row = 32 * grp + (t >> 4);
-    return (uint32_t)(key * 256 + (k_chunk(key, half_tile_chunk(t)) << 4)) |
-           ((uint32_t)(row * 256 + (v_chunk(row, t & 15) << 4)) << 16);
-  };
+  // LDS byte offset of this thread's K rows within a tile (kept live: it is
+  // cheaper than forming it twice per tile): chunks c and c + 8 differ in bit
+  // 3 of the swizzled chunk only (offset ^ 128)
+  const uint32_t kw0 = (uint32_t)((32 * grp + half_tile_key(gtid)) * 256 +
+                                  (k_chunk(32 * grp + half_tile_key(gtid), half_tile_chunk(gtid)) << 4));
   const uint32_t ug = (uint32_t)g;
   // floor(n / g) for the n = r + kt < g + 64 of the rotation table index,
   // without a division or a branch: the high word of n * ceil(2^32 / g), exact
@@ -1404,7 +1433,6 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       }
     }
   };
-  int v_slot = 0;  // (tile staged next) mod 3
   int ua_off = 0;       // this thread's small-angle row for the tile staged next (entries)
   f32x4 uar[2], bsr[2];  // the angle terms of pairs 4b .. 4b+3 (block b)
   float ylo[2], yhi[2];
@@ -1442,7 +1470,6 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
         }
       }
       if (i == 11) {
-        const uint32_t kw0 = write_offsets() & 0xffffu;
         uint8_t* skg = s_kg + (tt & 1) * kTileBytes;
         *reinterpret_cast<u32x4*>(skg + kw0) = kCached ? glo : regs.klo;
         *reinterpret_cast<u32x4*>(skg + (kw0 ^ 128u)) = kCached ? ghi : regs.khi;
@@ -1450,16 +1477,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     }
     if constexpr (kCached) {
       if (i == 11) {
-        const uint32_t kw0 = write_offsets() & 0xffffu;
         uint8_t* sk = s_k + (tt & 1) * kTileBytes;
         *reinterpret_cast<u32x4*>(sk + kw0) = regs.klo;
         *reinterpret_cast<u32x4*>(sk + (kw0 ^ 128u)) = regs.khi;
       }
-    }
-    if (i == 12) {
-      uint8_t* sv = s_v + v_slot * kTileBytes + (write_offsets() >> 16);
-      *reinterpret_cast<u32x4*>(sv) = regs.v0;
-      *reinterpret_cast<u32x4*>(sv + 16 * 256) = regs.v1;
     }
     if (i == 15) {
       // last, after any reload of the phase (a reload issued after these loads
@@ -1467,7 +1488,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       // than kept live through the loop
       int t = gtid;
       asm volatile("" : "+v"(t));
-      load_half(regs, kbase, vbase, kv_rs, n_kv, ld_t * kBN, stage_offsets(kv_rs, grp, t));
+      copy_v(tt + 1, ld_t * kBN);  // the V rows of tile tt + 1 into slot (tt + 1) & 3
+      load_k_only(regs, kbase, kv_rs, n_kv, ld_t * kBN, stage_offsets(kv_rs, grp, t));
     }
   };
   // this thread's small-angle row for a tile whose j0 mod g is r: c(j) =
@@ -1482,7 +1504,6 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   // after the staging of a tile: the next one's scalars
   auto next_stage = [&]() {
     advance_ld();
-    v_slot = v_slot == 2 ? 0 : v_slot + 1;
   };
   constexpr int kStageSteps = 16;
   using TT = std::true_type;
@@ -1530,9 +1551,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     __builtin_amdgcn_s_setprio(2);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (k & 1) * kTileBytes;
-    // V of tile k-1, slot (k - 1) mod 3 = (v_slot + 1) mod 3 (at tile 0 the
-    // probabilities are zero and tile 0's finite V is read)
-    const uint8_t* svp = s_v + (k > 0 ? (v_slot == 2 ? 0 : v_slot + 1) : 0) * kTileBytes;
+    // V of tile k-1 (at tile 0 the probabilities are zero and tile 0's finite V is read)
+    const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) & 3) * kTileBytes;
     if constexpr (KK == kInterior) {
       f32x16 sc[2];
       auto hook = [&](int i) {
@@ -1562,7 +1582,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
 #pragma unroll
       for (int i = 0; i < kStageSteps; ++i) stage_step(k + 1, i, RotT{}, CachedT{});
     }
-    __syncthreads();
+    lds_barrier();
     __builtin_amdgcn_s_setprio(0);
     // the row maxima belong to the VALU phase (the MFMA wave reaches the barrier
     // as soon as its last products are issued)
@@ -1583,7 +1603,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     if (gtid < 64) base_angles(k + 2);
     angle_row(ld_r);
     next_stage();
-    __syncthreads();
+    lds_barrier();
   };
 
   int k = 0;
@@ -1605,7 +1625,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     else tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kLocal>{});
   }
   for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{}, std::integral_constant<int, kLocal>{});
-  if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) % 3) * kTileBytes, lane_expand(lbase), pk, acc);
+  // the V copies of the tiles staged past the last are still in flight: none
+  // may land after the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (uses(ntiles - 1)) pv_tile<1>(s_v + ((ntiles - 1) & 3) * kTileBytes, lane_expand(lbase), pk, acc);
   if (grp == 0) __syncthreads();
 
   // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
