@@ -1340,8 +1340,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   // the group's half of a tile, two 16-byte copies per lane (lane l: row 4r +
   // l / 16, LDS position l % 16, so it fetches chunk v_chunk(row, l % 16))
   typedef __attribute__((address_space(3))) void lds_void;
-  auto copy_v = [&](int tt, int j0) {
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, kv_rs, n_kv, j0);
+  auto copy_v = [&](int tt, const __amdgpu_buffer_rsrc_t rv) {
     int t = lane;  // offsets formed here rather than kept live
     asm volatile("" : "+v"(t));
 #pragma unroll
@@ -1355,7 +1354,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   };
   HalfTile regs;
   const StageOffsets soff = stage_offsets(kv_rs, grp, gtid);
-  copy_v(0, 0);
+  copy_v(0, tile_rsrc(vbase, kv_rs, n_kv, 0));
   load_k_only(regs, kbase, kv_rs, n_kv, 0, soff);
 
   bf16x8 qf[8];
@@ -1422,9 +1421,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   const uint32_t r64 = (uint32_t)kBN % ug, q64 = (uint32_t)kBN / ug;
   int ld_t = 0;
   uint32_t ld_r = 0, ld_q = 0;
+  const uint16_t* ld_k = kbase;  // the tile's first K and V rows
+  const uint16_t* ld_v = vbase;
   auto advance_ld = [&]() {
     if (ld_t < ntiles - 1) {
       ++ld_t;
+      ld_k += kBN * kv_rs;
+      ld_v += kBN * kv_rs;
       ld_r += r64;
       ld_q += q64;
       if (ld_r >= ug) {
@@ -1488,8 +1491,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       // than kept live through the loop
       int t = gtid;
       asm volatile("" : "+v"(t));
-      copy_v(tt + 1, ld_t * kBN);  // the V rows of tile tt + 1 into slot (tt + 1) & 3
-      load_k_only(regs, kbase, kv_rs, n_kv, ld_t * kBN, stage_offsets(kv_rs, grp, t));
+      // buffer resources over the tile's rows that exist (rows past n_kv read zeros)
+      const int nbytes = (int)(min(kBN, n_kv - ld_t * kBN) * kv_rs * 2);
+      copy_v(tt + 1, __builtin_amdgcn_make_buffer_rsrc((void*)ld_v, (short)0, nbytes, 0x00020000));
+      const StageOffsets so = stage_offsets(kv_rs, grp, t);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)ld_k, (short)0, nbytes, 0x00020000);
+      regs.klo = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k, 0, 0);
+      regs.khi = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k + 128, 0, 0);
     }
   };
   // this thread's small-angle row for a tile whose j0 mod g is r: c(j) =
