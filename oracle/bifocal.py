@@ -497,10 +497,10 @@ def bifocal_bruteforce(q_raw, k_raw, v, pretrained_window, local_window, rope_ba
     explicit D x D rotation matrices; for tiny inputs only.
 
     For each causal pair (i, j), j <= p_i: the local rule keeps the original
-    positions (p_i, j) when p_i - j <= W-1 (ResearchPod transcript: recent text
-    keeps the original compass settings); otherwise both positions are aliased
-    to (p_i // g, j // g) (ResearchPod transcript: a distant position is mapped
-    onto a point of the grid the model knows).  Score
+    positions (p_i, j) when p_i - j <= W-1 (ResearchPod transcript: nearby text
+    keeps its original rotations); otherwise both positions are aliased to
+    (p_i // g, j // g) (ResearchPod transcript: a far position is snapped to a
+    coarser grid of positions seen in training).  Score
     ``tau * (R(P_q theta) q_i) . (R(P_k theta) k_j)``, explicit softmax over the
     row, output ``sum_j P_ij v_j``.
 
