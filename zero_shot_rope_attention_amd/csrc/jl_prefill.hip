@@ -140,17 +140,38 @@ __device__ __forceinline__ LaneOffsets lane_expand(const LaneBase& b) {
   return o;
 }
 
+// Byte offsets of K fragment kk and V^T column block nb, from either form.
+__device__ __forceinline__ int k_off(const LaneOffsets& o, int kk) { return o.k[kk]; }
+__device__ __forceinline__ int v_off(const LaneOffsets& o, int nb) { return o.v[nb]; }
+__device__ __forceinline__ int k_off(const LaneBase& b, int kk) { return (int)(b.k0 ^ ((uint32_t)kk << 5)); }
+__device__ __forceinline__ int v_off(const LaneBase& b, int nb) { return (int)(b.v0 ^ ((uint32_t)nb << 6)); }
+
+// S^T of one 32-key block (rows kbuf .. kbuf + 32 keys) against the query fragment.
+// kLean: each step's operand is read in that step (a scheduling barrier after
+// every product), for code outside the hot loop where registers are short.
+template <bool kLean = false, class LO>
+__device__ __forceinline__ f32x16 qk_block(const uint8_t* kbuf, const LO& lo, const bf16x8 (&q)[8]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(kbuf + k_off(lo, kk))), q[kk], acc);
+    if constexpr (kLean) __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
 // S^T tile (64 keys x 32 query rows) from a K tile in LDS and the query
 // fragment; the two 32-key blocks accumulate side by side.
-__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const LaneOffsets& lo, const bf16x8 (&qf)[8],
-                                        f32x16 (&s)[2]) {
+template <bool kLean = false, class LO>
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const LO& lo, const bf16x8 (&qf)[8], f32x16 (&s)[2]) {
   f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(kbuf + lo.k[kk]);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(kbuf + lo.k[kk] + 32 * 256);
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(kbuf + k_off(lo, kk));
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(kbuf + k_off(lo, kk) + 32 * 256);
     acc0 = mfma32(as_bf16x8(a0), qf[kk], acc0);
     acc1 = mfma32(as_bf16x8(a1), qf[kk], acc1);
+    if constexpr (kLean) __builtin_amdgcn_sched_barrier(0);
   }
   s[0] = acc0;
   s[1] = acc1;
@@ -237,8 +258,8 @@ __device__ __forceinline__ void store_k(const KRegs<512 / NT>& r, uint8_t* sk, u
 // entries are -inf.  Lane (h, n) gets row n, keys j0 + 32kb + 16h + i.
 // kInterior: every key of the tile is causal for every row of the workgroup and,
 // in the bifocal mode, remote for every row -- no masks, grouped scores only.
-template <int MODE, bool kInterior, int NS>
-__device__ __forceinline__ void tile_scores(const uint8_t* sk, const uint8_t* skg, const LaneOffsets& lo,
+template <int MODE, bool kInterior, int NS, bool kLean = false, class LO>
+__device__ __forceinline__ void tile_scores(const uint8_t* sk, const uint8_t* skg, const LO& lo,
                                             const bf16x8 (&qf)[8], const bf16x8 (&qg)[8], int lane, int j0,
                                             int my_p, int w, bool use_base, bool use_grp, float (&x)[NS][2][16]) {
   const int h = lane >> 5;
@@ -251,35 +272,34 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sk, const uint8_t* sk
       for (int i = 0; i < 16; ++i) x[0][kb][i] = sc[kb][i];
   } else if constexpr (MODE == kModePlain) {
     f32x16 sb[2];
-    qk_tile(sk, lo, qf, sb);
+    qk_tile<kLean>(sk, lo, qf, sb);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         x[0][kb][i] = (my_p - (j0 + 32 * kb + 16 * h + i) >= 0) ? sb[kb][i] : -INFINITY;
   } else if constexpr (MODE == kModeBifocal) {
-    // remote keys take grouped scores, local keys base scores
-    if (use_grp) {
-      f32x16 sg[2];
-      qk_tile(skg, lo, qg, sg);
+    // remote keys take grouped scores, local keys base scores; one 32-key block
+    // at a time, so that only one block's products of each kind are live
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      if (use_grp) {
+        const f32x16 sg = qk_block<kLean>(skg + kb * 32 * 256, lo, qg);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          x[0][kb][i] = (my_p - (j0 + 32 * kb + 16 * h + i) >= 0) ? sg[kb][i] : -INFINITY;
-    }
-    if (use_base) {
-      f32x16 sb[2];
-      qk_tile(sk, lo, qf, sb);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < 16; ++i) x[0][kb][i] = (my_p - (j0 + 32 * kb + 16 * h + i) >= 0) ? sg[i] : -INFINITY;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (use_base) {
+        const f32x16 sb = qk_block<kLean>(sk + kb * 32 * 256, lo, qf);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int dist = my_p - (j0 + 32 * kb + 16 * h + i);
           const bool local = dist >= 0 && dist < w;
           const float other = use_grp ? x[0][kb][i] : -INFINITY;
-          x[0][kb][i] = local ? sb[kb][i] : other;
+          x[0][kb][i] = local ? sb[i] : other;
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   } else {
     f32x16 sb[2], sg[2];
@@ -364,12 +384,12 @@ __device__ __forceinline__ void softmax_exp(const float (&x)[NS][2][16], const f
 // The V^T operand (lane (n, h): d = 32nb + n, 8 keys) comes from two
 // transposed reads of the row-major V tile: lane j of each 16-lane group reads
 // 4 values of d at key 4r + j/4 (r = 0, 1), columns 4(j % 4) .. 4(j % 4) + 3.
-template <int NS>
-__device__ __forceinline__ void pv_tile(const uint8_t* sv, const LaneOffsets& lo, const uint32_t (&pk)[NS][2][8],
+template <int NS, bool kLean = false, class LO = LaneOffsets>
+__device__ __forceinline__ void pv_tile(const uint8_t* sv, const LO& lo, const uint32_t (&pk)[NS][2][8],
                                         f32x16 (&acc)[NS][4]) {
   const lds_byte* vp[4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) vp[nb] = lds_opaque(lds_ptr(sv) + lo.v[nb]);
+  for (int nb = 0; nb < 4; ++nb) vp[nb] = lds_opaque(lds_ptr(sv) + v_off(lo, nb));
 #pragma unroll
   for (int step = 0; step < 4; ++step) {
     const int kb = step >> 1, half = step & 1;
@@ -384,6 +404,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* sv, const LaneOffsets& lo
                           pk[s][kb][4 * half + 3]};
         acc[s][nb] = mfma32(as_bf16x8(vf), as_bf16x8(pf), acc[s][nb]);
       }
+      if constexpr (kLean) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -1357,16 +1378,17 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   copy_v(0, tile_rsrc(vbase, kv_rs, n_kv, 0));
   load_k_only(regs, kbase, kv_rs, n_kv, 0, soff);
 
-  bf16x8 qf[8];
-  bf16x8 qg[8];
-  {
-    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
-    u32x4 raw[8];
+  // this lane's share of its query row as stored (the address made opaque, so
+  // that the loads stay where they are written)
+  auto load_qraw = [&](u32x4 (&raw)[8]) {
+    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD + 8 * h;
+    asm volatile("" : "+v"(qrow));
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      raw[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
-      qf[kk] = as_bf16x8(raw[kk]);
-    }
+    for (int kk = 0; kk < 8; ++kk)
+      raw[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0, 0, 0, 0};
+  };
+  // q^g = rot(q, c(p) theta), rounded to bf16
+  auto correct_q = [&](const u32x4 (&raw)[8], bf16x8 (&dst)[8]) {
     const long long cq = row_ok ? (long long)(my_p / g) - my_p + SEQ_Q_SHIFT : 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -1385,9 +1407,16 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
         lo[e2] = pack_bf16(y1[0], y1[1]);
         hi[e2] = pack_bf16(y2[0], y2[1]);
       }
-      qg[kk] = as_bf16x8(lo);
-      qg[kk + 4] = as_bf16x8(hi);
+      dst[kk] = as_bf16x8(lo);
+      dst[kk + 4] = as_bf16x8(hi);
     }
+  };
+  bf16x8 qf[8];  // the base-RoPE query fragment: local tiles only
+  bf16x8 qg[8];  // the corrected one: interior and edge tiles
+  {
+    u32x4 raw[8];
+    load_qraw(raw);
+    correct_q(raw, qg);
   }
 
   // ---- staging of this group's half of tile tt: 16 steps, run one per MFMA
@@ -1439,7 +1468,6 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   int ua_off = 0;       // this thread's small-angle row for the tile staged next (entries)
   f32x4 uar[2], bsr[2];  // the angle terms of pairs 4b .. 4b+3 (block b)
   float ylo[2], yhi[2];
-  u32x4 glo, ghi;
   auto base_angles = [&](int tt) {  // rotation base of tile ld_t, by the group's first 64 threads
     s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rev_reduce((int)ld_q - ld_t * kBN, s_theta[gtid]);
   };
@@ -1465,21 +1493,20 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
         yhi[e & 1] = yr.y;
         if (e & 1) {
           // pairs e-1 and e came from word e/2 of each half: the corrected pair
-          // replaces it in place unless the keys as cached are stored too
-          u32x4& dlo = kCached ? glo : regs.klo;
-          u32x4& dhi = kCached ? ghi : regs.khi;
-          dlo[e >> 1] = pack_bf16(ylo[0], ylo[1]);
-          dhi[e >> 1] = pack_bf16(yhi[0], yhi[1]);
+          // replaces it in place (the keys as cached, where needed, are already
+          // in LDS)
+          regs.klo[e >> 1] = pack_bf16(ylo[0], ylo[1]);
+          regs.khi[e >> 1] = pack_bf16(yhi[0], yhi[1]);
         }
       }
       if (i == 11) {
         uint8_t* skg = s_kg + (tt & 1) * kTileBytes;
-        *reinterpret_cast<u32x4*>(skg + kw0) = kCached ? glo : regs.klo;
-        *reinterpret_cast<u32x4*>(skg + (kw0 ^ 128u)) = kCached ? ghi : regs.khi;
+        *reinterpret_cast<u32x4*>(skg + kw0) = regs.klo;
+        *reinterpret_cast<u32x4*>(skg + (kw0 ^ 128u)) = regs.khi;
       }
     }
     if constexpr (kCached) {
-      if (i == 11) {
+      if (i == 0) {  // before the rotation overwrites them
         uint8_t* sk = s_k + (tt & 1) * kTileBytes;
         *reinterpret_cast<u32x4*>(sk + kw0) = regs.klo;
         *reinterpret_cast<u32x4*>(sk + (kw0 ^ 128u)) = regs.khi;
@@ -1551,6 +1578,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   if (grp == 1) __syncthreads();  // group B runs one phase behind
 
   constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
+
   // tile k of kind KK, staging tile k + 1 of kind KT
   auto tile = [&](int k, auto kk_tag, auto kt_tag) {
     constexpr int KK = decltype(kk_tag)::value, KT = decltype(kt_tag)::value;
@@ -1579,14 +1607,25 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
         if constexpr (KK == kEdge) {
           const bool use_grp = j0 <= wp_hi - w;
           const bool use_base = j0 + kBN - 1 >= wp_lo - w + 1;
-          tile_scores<kModeBifocal, false, 1>(sk, skg, lane_expand(lbase), qf, qg, lane, j0, my_p, w, use_base,
-                                              use_grp, xs);
+          // an edge tile (one or two per workgroup) reads the base-RoPE query
+          // fragment afresh: it and the corrected one do not both fit in
+          // registers across the band
+          bf16x8 qfe[8];
+          {
+            u32x4 raw[8];
+            load_qraw(raw);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) qfe[kk] = as_bf16x8(raw[kk]);
+          }
+          tile_scores<kModeBifocal, false, 1, true>(sk, skg, lbase, qfe, qg, lane, j0, my_p, w, use_base, use_grp,
+                                                    xs);
         } else {
-          tile_scores<kModePlain, false, 1>(sk, skg, lane_expand(lbase), qf, qg, lane, j0, my_p, w, true, false,
-                                            xs);
+          tile_scores<kModePlain, false, 1>(sk, skg, lbase, qf, qg, lane, j0, my_p, w, true, false, xs);
         }
       }
-      if (k > 0 && uses(k - 1)) pv_tile<1>(svp, lane_expand(lbase), pk, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k > 0 && uses(k - 1)) pv_tile<1, KK == kEdge>(svp, lbase, pk, acc);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kStageSteps; ++i) stage_step(k + 1, i, RotT{}, CachedT{});
     }
@@ -1621,16 +1660,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     else tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kLocal>{});
     ++k;
   }
-  {
-    // the base-RoPE query fragment is only needed from the band on
-    const uint16_t* qrow = a.q + (SEQ_Q0 + (row_ok ? my_row : 0)) * q_rs + (int64_t)hq * kD;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0});
-  }
   for (; k < t_local; ++k) {
     if (k + 1 < t_local) tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kEdge>{});
     else tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kLocal>{});
+  }
+  {
+    u32x4 raw[8];
+    load_qraw(raw);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(raw[kk]);
   }
   for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{}, std::integral_constant<int, kLocal>{});
   // the V copies of the tiles staged past the last are still in flight: none
