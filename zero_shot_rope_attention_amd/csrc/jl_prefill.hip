@@ -1235,9 +1235,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 // spread over the steps of the MFMA sequence.  A wave issues about one
 // instruction per 4-5 cycles whatever its kind, so a VALU phase holding both
 // the softmax and the rotation outlasts the other group's MFMA phase, whose
-// wave leaves most of its own issue slots idle between MFMAs.  What the
-// rotation needs first (the tile's rotation base and each thread's row of the
-// small-angle table) is prepared in the VALU phase before, which has slack.
+// wave leaves most of its own issue slots idle between MFMAs.  The keys'
+// angles themselves (the tile's rotation base plus each key's small-angle
+// table entry) are formed in the VALU phase before, which has slack.
 //
 // A key's angle c(j) theta_d = c(j0) theta_d - u theta_d, u = j - j0 - (floor(j
 // / g) - floor(j0 / g)) < 64: the tile's base angle (exact integer c(j0), fp64
@@ -1249,16 +1249,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
 //         group's half of tile k+1's keys into LDS (corrected, and as cached
 //         for band tiles), then its half of tile k+2: the V rows copied
 //         straight from memory into LDS, the keys loaded into registers.
-//   V(k): the softmax of tile k, then tile k+2's rotation base and each
-//         thread's small-angle row for it.
+//   V(k): the softmax of tile k, then tile k+3's rotation base and each
+//         thread's 8 key angles of tile k+2.
 // Tile k+1's keys are written in M(k) by both groups into the K / K^g buffers
 // of tile k-1, last read in M(k-1) of both groups.  V rows sit in four slots
 // (tile & 3): tile k+2's copies land in the slot of tile k-2, last read in
 // M(k-1), and are complete (each wave waits for them with its key loads in
 // M(k+1)) two phases before M(k+3) first reads them; the loop's barriers wait
 // for LDS operations only, so the copies stay in flight across them.  Rotation
-// bases sit in two slots per group (tile & 1): tile k+2's is written in V(k),
-// the slot of tile k, whose staging in M(k-1) read it last.  Staging past the
+// bases sit in four slots per group (tile & 3): tile k+3's is written in V(k)
+// into the slot of tile k-1, whose angles were formed in V(k-3), and read in
+// V(k+1), after the barriers between.  Staging past the
 // last tile re-stages the last one into slots no later phase reads, so the
 // loop has no branches.
 // ---------------------------------------------------------------------------
@@ -1275,7 +1276,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   uint8_t* const s_kg = s_tiles + 2 * kTileBytes;
   uint8_t* const s_v = s_vt;
   __shared__ __attribute__((aligned(16))) float s_uang[64 * kUangStride];  // -u theta_d in revolutions, u < 64
-  __shared__ __attribute__((aligned(16))) float s_base[4 * kHalfD];        // c(j0) theta_d, revolutions: [group][tile & 1]
+  __shared__ __attribute__((aligned(16))) float s_base[8 * kHalfD];        // c(j0) theta_d, revolutions: [group][tile & 3]
   __shared__ double s_theta[kHalfD];                                        // theta_d / (2 pi)
 
   const int tid = threadIdx.x;
@@ -1468,26 +1469,28 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       }
     }
   };
-  int ua_off = 0;       // this thread's small-angle row for the tile staged next (entries)
-  f32x4 uar[2], bsr[2];  // the angle terms of pairs 4b .. 4b+3 (block b)
+  float ang8[8];  // this thread's 8 key angles (revolutions) for the tile staged next
   float ylo[2], yhi[2];
-  auto base_angles = [&](int tt) {  // rotation base of tile ld_t, by the group's first 64 threads
-    s_base[(2 * grp + (tt & 1)) * kHalfD + gtid] = rev_reduce((int)ld_q - ld_t * kBN, s_theta[gtid]);
+  // rotation base of tile tt (clamped to the last tile) into slot tt & 3, by
+  // the group's first 64 threads; q = floor(64 t / g)
+  auto base_angles = [&](int tt, int t_c, uint32_t q_c) {
+    int t = gtid;  // the address formed here rather than kept live
+    asm volatile("" : "+v"(t));
+    s_base[(4 * grp + (tt & 3)) * kHalfD + t] = rev_reduce((int)q_c - t_c * kBN, s_theta[t]);
+  };
+  // the tile after ld_t (clamped), one tile ahead of the angle preparation
+  auto base_ahead = [&](int tt) {
+    const bool more = ld_t < ntiles - 1;
+    const uint32_t q1 = ld_q + (more ? q64 + (ld_r + r64 >= ug ? 1u : 0u) : 0u);
+    base_angles(tt, more ? ld_t + 1 : ld_t, q1);
   };
   // kRot: tile tt needs corrected keys; kCached: it needs the keys as cached
   auto stage_step = [&](int tt, int i, auto rot_tag, auto cached_tag) {
     constexpr bool kRot = decltype(rot_tag)::value, kCached = decltype(cached_tag)::value;
     if constexpr (kRot) {
-      if (i == 0 || i == 6) {  // the angle terms of pairs 4b .. 4b+3: a 16-byte read per table
-        const int b = i == 0 ? 0 : 1;
-        const float* ua = s_uang + ua_off;
-        const float* bs = s_base + (2 * grp + (tt & 1)) * kHalfD + 8 * kc;
-        uar[b] = *reinterpret_cast<const f32x4*>(ua + 4 * b);
-        bsr[b] = *reinterpret_cast<const f32x4*>(bs + 4 * b);
-      }
       if (i & 1) {  // pair e = (i - 1) / 2 on every other step: c(j0) theta_d - u theta_d
         const int e = i >> 1;
-        const float ang = bsr[e >> 2][e & 3] + uar[e >> 2][e & 3];
+        const float ang = ang8[e];
         const f32x2 cs = {__builtin_amdgcn_cosf(ang), __builtin_amdgcn_sinf(ang)};
         const f32x2 yr = rot_pair(elem(regs.klo, e), elem(regs.khi, e), cs.x, cs.y);
         ylo[e & 1] = yr.x;
@@ -1528,14 +1531,23 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       regs.khi = __builtin_amdgcn_raw_buffer_load_b128(rk, so.k + 128, 0, 0);
     }
   };
-  // this thread's small-angle row for a tile whose j0 mod g is r: c(j) =
-  // c(j0) - u with u = kt - floor((r + kt) / g)
-  auto angle_row = [&](uint32_t r) {
+  // this thread's 8 key angles for tile tt, whose j0 mod g is r: the tile's
+  // rotation base (slot tt & 3) plus the small-angle row of c(j) = c(j0) - u,
+  // u = kt - floor((r + kt) / g)
+  auto angle_row = [&](int tt, uint32_t r) {
     int t = gtid;  // kt formed here rather than kept live
     asm volatile("" : "+v"(t));
     const int key = 32 * grp + half_tile_key(t);
     const int u = key - (int)floor_div_g(r + (uint32_t)key);
-    ua_off = u * kUangStride + 8 * kc;
+    const float* ua = s_uang + u * kUangStride + 8 * kc;
+    const float* bs = s_base + (4 * grp + (tt & 3)) * kHalfD + 8 * kc;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x4 uv = *reinterpret_cast<const f32x4*>(ua + 4 * b);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bs + 4 * b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ang8[4 * b + e] = bv[e] + uv[e];
+    }
   };
   // after the staging of a tile: the next one's scalars
   auto next_stage = [&]() {
@@ -1545,21 +1557,26 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   using TT = std::true_type;
   using FF = std::false_type;
 
-  // ---- prologue: tile 0 staged, the loads, rotation base and angle row of
-  // tile 1 ----
+  // ---- prologue: the rotation bases of tiles 0-2, tile 0 staged, the loads
+  // and the key angles of tile 1 ----
   __syncthreads();  // theta table
-  if (gtid < 64) base_angles(0);
-  advance_ld();  // the prologue's loads and rotation base are tile 1's
+  if (gtid < 64) {  // rotation bases of tiles 0, 1, 2
+#pragma unroll 1
+    for (int t = 0; t < 3; ++t) {
+      const int t_c = min(t, ntiles - 1);
+      base_angles(t, t_c, (uint32_t)(t_c * kBN) / ug);
+    }
+  }
+  advance_ld();  // the prologue's loads are tile 1's
   __syncthreads();
-  angle_row(0u);
+  angle_row(0, 0u);
 #pragma unroll
   for (int i = 0; i < kStageSteps; ++i) {
     if (n_interior > 0) stage_step(0, i, TT{}, FF{});
     else if (t_local > 0) stage_step(0, i, TT{}, TT{});
     else stage_step(0, i, FF{}, TT{});
   }
-  if (gtid < 64) base_angles(1);
-  angle_row(ld_r);
+  angle_row(1, ld_r);
   next_stage();
 
   const LaneBase lbase = lane_base(lane);
@@ -1643,13 +1660,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       softmax_max<1>(xs, m_run, l_run, acc, scale_log2);
       softmax_exp<1, false>(xs, m_run, l_run, scale_log2, pk);
     }
-    // for tile k+2, staged in the next MFMA phase: its rotation base (slot
-    // (k+2) & 1, last read when tile k was staged), by the group's first wave,
-    // and each thread's small-angle row (its r is ld_r).  This phase has slack;
-    // in the MFMA phase that one wave's extra work and the row's dependent reads
-    // held back the barrier
-    if (gtid < 64) base_angles(k + 2);
-    angle_row(ld_r);
+    // tile k+3's rotation base, by the group's first wave, and for tile k+2,
+    // staged in the next MFMA phase, each thread's 8 key angles (its r is
+    // ld_r).  This phase has slack; in the MFMA phase the table reads and the
+    // additions measured about 1% slower
+    if (gtid < 64) base_ahead(k + 3);
+    angle_row(k + 2, ld_r);
     next_stage();
     lds_barrier();
   };
