@@ -1187,7 +1187,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     for (; k < t_local; ++k) tile(k, std::integral_constant<int, kEdge>{});
   if constexpr (kPre || kSliding) {
     // local tiles below the workgroup's first row need no mask, as in plain mode
-    // (not in the fused bifocal kernel, whose interior loop has no registers to spare)
     const int t_free = min(ntiles, max(k, (p0_wg + 1) / kBN));
     if constexpr (kPre) {
       // the base query fragment afresh: the copy from before the edge tiles, where
@@ -1595,26 +1594,31 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   __syncthreads();
   if (grp == 1) __syncthreads();  // group B runs one phase behind
 
-  constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
+  // kLocalFree: a local tile whose keys are causal for every row of the
+  // workgroup (below its first row), which needs no mask
+  constexpr int kInterior = 0, kEdge = 1, kLocal = 2, kLocalFree = 3;
 
   // tile k of kind KK, staging tile k + 1 of kind KT
   auto tile = [&](int k, auto kk_tag, auto kt_tag) {
     constexpr int KK = decltype(kk_tag)::value, KT = decltype(kt_tag)::value;
-    using RotT = std::integral_constant<bool, KT != kLocal>;
+    using RotT = std::integral_constant<bool, KT != kLocal && KT != kLocalFree>;
     using CachedT = std::integral_constant<bool, KT != kInterior>;
     __builtin_amdgcn_s_setprio(2);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (k & 1) * kTileBytes;
     // V of tile k-1 (at tile 0 the probabilities are zero and tile 0's finite V is read)
     const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) & 3) * kTileBytes;
-    if constexpr (KK == kInterior) {
+    if constexpr (KK == kInterior || KK == kLocalFree) {
       f32x16 sc[2];
       auto hook = [&](int i) {
         if (i < kStageSteps) stage_step(k + 1, i, RotT{}, CachedT{});
       };
       // operands read one step ahead: the staging work makes a step long enough
-      // to cover the LDS latency, and the two registers sets saved are needed
-      mphase_compact(skg, svp, lbase, qg, pk, sc, acc, hook);
+      // to cover the LDS latency, and the two registers sets saved are needed.
+      // Interior tiles take the corrected keys and query, unmasked local tiles
+      // the keys as cached and the base-RoPE query.
+      if constexpr (KK == kInterior) mphase_compact(skg, svp, lbase, qg, pk, sc, acc, hook);
+      else mphase_compact(sk, svp, lbase, qf, pk, sc, acc, hook);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1656,7 +1660,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
 #pragma unroll
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xs[0][kb][i]));
     // ---- V(k): softmax of tile k ----
-    if (KK == kInterior || uses(k)) {
+    if (KK == kInterior || KK == kLocalFree || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, scale_log2);
       softmax_exp<1, false>(xs, m_run, l_run, scale_log2, pk);
     }
@@ -1686,6 +1690,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     load_qraw(raw);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(raw[kk]);
+  }
+  {
+    const int t_free = min(ntiles, max(k, (p0_wg + 1) / kBN));
+    for (; k < t_free; ++k) {
+      if (k + 1 < t_free) tile(k, std::integral_constant<int, kLocalFree>{}, std::integral_constant<int, kLocalFree>{});
+      else tile(k, std::integral_constant<int, kLocalFree>{}, std::integral_constant<int, kLocal>{});
+    }
   }
   for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{}, std::integral_constant<int, kLocal>{});
   // the V copies of the tiles staged past the last are still in flight: none
