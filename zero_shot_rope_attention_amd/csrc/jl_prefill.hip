@@ -1421,11 +1421,11 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
 
   // ---- staging of this group's half of tile tt: 16 steps, run one per MFMA
   // step of an interior tile's MFMA phase, or back to back otherwise: the keys
-  // as cached where needed (step 0), the angle terms of four pairs each (steps
-  // 0 and 6), one corrected pair on every odd step, and at step 15 the
-  // corrected keys' LDS writes and the next tile's V copies and key loads.
-  // Spreading the rotations over the phase, the reads a few steps ahead of
-  // their use, measured about 1% faster than eight consecutive steps ----
+  // as cached where needed (step 0), one corrected pair on every odd step (its
+  // angle formed in the VALU phase before), and at step 15 the corrected keys'
+  // LDS writes and the next tile's V copies and key loads.  Spreading the
+  // rotations over the phase measured about 1% faster than eight consecutive
+  // steps ----
   // this thread: key kt = 32 grp + gtid / 8 of the tile, rotate-half pairs 8c .. 8c+7
   const int kc = half_tile_chunk(gtid);
   // LDS byte offset of this thread's K rows within a tile (kept live: it is
@@ -1446,10 +1446,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   auto floor_div_g = [&](uint32_t n) -> uint32_t {
     return __umulhi(n, g_magic) + n * g_one + (n >= g_cmp ? 1u : 0u);
   };
-  // per-tile scalars, advanced once per tile: the tile whose loads, rotation
-  // base and angle rows are prepared next (ld_t, its j0 = 64 ld_t, ld_r = j0
-  // mod g, ld_q = floor(j0 / g)); ld_t stops at the last tile (staging past it
-  // re-stages the last tile into unread slots)
+  // per-tile scalars, advanced once per tile: the tile whose loads and key
+  // angles are prepared next (ld_t, its j0 = 64 ld_t, ld_r = j0 mod g, ld_q =
+  // floor(j0 / g)); ld_t stops at the last tile (staging past it re-stages the
+  // last tile into unread slots)
   const uint32_t r64 = (uint32_t)kBN % ug, q64 = (uint32_t)kBN / ug;
   int ld_t = 0;
   uint32_t ld_r = 0, ld_q = 0;
