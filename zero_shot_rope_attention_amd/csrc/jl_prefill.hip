@@ -1350,6 +1350,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     t_local = first_all_local <= 0 ? 0 : (first_all_local + kBN - 1) / kBN;
     t_local = min(ntiles, max(n_interior, t_local));
   }
+  // local tiles below the workgroup's first row (every key causal for every
+  // row) need no mask: they run the interior tiles' code on the keys staged
+  // with a zero rotation (so exactly as cached) and the base-RoPE query
+  const int t_free = min(ntiles, max(t_local, (p0_wg + 1) / kBN));
 
   // tables first, while few values are live
   if (tid < kHalfD) s_theta[tid] = SEQ_THETA(tid);
@@ -1411,8 +1415,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
       dst[kk + 4] = as_bf16x8(hi);
     }
   };
-  bf16x8 qf[8];  // the base-RoPE query fragment: local tiles only
-  bf16x8 qg[8];  // the corrected one: interior and edge tiles
+  // the query fragment: corrected (interior and edge tiles), then base-RoPE
+  // (local tiles; edge tiles read that one afresh)
+  bf16x8 qg[8];
   {
     u32x4 raw[8];
     load_qraw(raw);
@@ -1445,6 +1450,11 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   const uint32_t g_cmp = ug > kMagicMaxG ? ug : 0xffffffffu;
   auto floor_div_g = [&](uint32_t n) -> uint32_t {
     return __umulhi(n, g_magic) + n * g_one + (n >= g_cmp ? 1u : 0u);
+  };
+  // the same with g = 1's scalars for local tiles (zero rotation: u = 0)
+  auto floor_div_sel = [&](uint32_t n, bool zero) -> uint32_t {
+    const uint32_t gm = zero ? 0u : g_magic, go = zero ? 1u : g_one, gc = zero ? 0xffffffffu : g_cmp;
+    return __umulhi(n, gm) + n * go + (n >= gc ? 1u : 0u);
   };
   // per-tile scalars, advanced once per tile: the tile whose loads and key
   // angles are prepared next (ld_t, its j0 = 64 ld_t, ld_r = j0 mod g, ld_q =
@@ -1480,8 +1490,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   // the tile after ld_t (clamped), one tile ahead of the angle preparation
   auto base_ahead = [&](int tt) {
     const bool more = ld_t < ntiles - 1;
+    const int t1 = more ? ld_t + 1 : ld_t;
     const uint32_t q1 = ld_q + (more ? q64 + (ld_r + r64 >= ug ? 1u : 0u) : 0u);
-    base_angles(tt, more ? ld_t + 1 : ld_t, q1);
+    // local tiles: base 0 (c = q - 64 t is zeroed)
+    base_angles(tt, t1, t1 >= t_local ? (uint32_t)(t1 * kBN) : q1);
   };
   // kRot: tile tt needs corrected keys; kCached: it needs the keys as cached
   auto stage_step = [&](int tt, int i, auto rot_tag, auto cached_tag) {
@@ -1537,7 +1549,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     int t = gtid;  // kt formed here rather than kept live
     asm volatile("" : "+v"(t));
     const int key = 32 * grp + half_tile_key(t);
-    const int u = key - (int)floor_div_g(r + (uint32_t)key);
+    const bool zero = min(tt, ntiles - 1) >= t_local;  // a local tile: u = 0, base 0
+    const int u = key - (int)floor_div_sel((zero ? 0u : r) + (uint32_t)key, zero);
     const float* ua = s_uang + u * kUangStride + 8 * kc;
     const float* bs = s_base + (4 * grp + (tt & 3)) * kHalfD + 8 * kc;
 #pragma unroll
@@ -1563,7 +1576,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
 #pragma unroll 1
     for (int t = 0; t < 3; ++t) {
       const int t_c = min(t, ntiles - 1);
-      base_angles(t, t_c, (uint32_t)(t_c * kBN) / ug);
+      base_angles(t, t_c, t_c >= t_local ? (uint32_t)(t_c * kBN) : (uint32_t)(t_c * kBN) / ug);
     }
   }
   advance_ld();  // the prologue's loads are tile 1's
@@ -1571,7 +1584,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   angle_row(0, 0u);
 #pragma unroll
   for (int i = 0; i < kStageSteps; ++i) {
-    if (n_interior > 0) stage_step(0, i, TT{}, FF{});
+    if (n_interior > 0 || (t_local == 0 && t_free > 0)) stage_step(0, i, TT{}, FF{});
     else if (t_local > 0) stage_step(0, i, TT{}, TT{});
     else stage_step(0, i, FF{}, TT{});
   }
@@ -1594,31 +1607,28 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
   __syncthreads();
   if (grp == 1) __syncthreads();  // group B runs one phase behind
 
-  // kLocalFree: a local tile whose keys are causal for every row of the
-  // workgroup (below its first row), which needs no mask
-  constexpr int kInterior = 0, kEdge = 1, kLocal = 2, kLocalFree = 3;
+  constexpr int kInterior = 0, kEdge = 1, kLocal = 2;
 
   // tile k of kind KK, staging tile k + 1 of kind KT
   auto tile = [&](int k, auto kk_tag, auto kt_tag) {
     constexpr int KK = decltype(kk_tag)::value, KT = decltype(kt_tag)::value;
-    using RotT = std::integral_constant<bool, KT != kLocal && KT != kLocalFree>;
+    using RotT = std::integral_constant<bool, KT != kLocal>;
     using CachedT = std::integral_constant<bool, KT != kInterior>;
     __builtin_amdgcn_s_setprio(2);
     const uint8_t* sk = s_k + (k & 1) * kTileBytes;
     const uint8_t* skg = s_kg + (k & 1) * kTileBytes;
     // V of tile k-1 (at tile 0 the probabilities are zero and tile 0's finite V is read)
     const uint8_t* svp = s_v + ((k > 0 ? k - 1 : 0) & 3) * kTileBytes;
-    if constexpr (KK == kInterior || KK == kLocalFree) {
+    if constexpr (KK == kInterior) {
       f32x16 sc[2];
       auto hook = [&](int i) {
         if (i < kStageSteps) stage_step(k + 1, i, RotT{}, CachedT{});
       };
       // operands read one step ahead: the staging work makes a step long enough
       // to cover the LDS latency, and the two registers sets saved are needed.
-      // Interior tiles take the corrected keys and query, unmasked local tiles
-      // the keys as cached and the base-RoPE query.
-      if constexpr (KK == kInterior) mphase_compact(skg, svp, lbase, qg, pk, sc, acc, hook);
-      else mphase_compact(sk, svp, lbase, qf, pk, sc, acc, hook);
+      // (Unmasked local tiles come here too: their keys were staged into the
+      // corrected buffer with a zero rotation, and qg then holds the base query.)
+      mphase_compact(skg, svp, lbase, qg, pk, sc, acc, hook);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1642,7 +1652,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
           tile_scores<kModeBifocal, false, 1, true>(sk, skg, lbase, qfe, qg, lane, j0, my_p, w, use_base, use_grp,
                                                     xs);
         } else {
-          tile_scores<kModePlain, false, 1>(sk, skg, lbase, qf, qg, lane, j0, my_p, w, true, false, xs);
+          tile_scores<kModePlain, false, 1>(sk, skg, lbase, qg, qg, lane, j0, my_p, w, true, false, xs);  // qg: base-RoPE by then
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1660,7 +1670,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
 #pragma unroll
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xs[0][kb][i]));
     // ---- V(k): softmax of tile k ----
-    if (KK == kInterior || KK == kLocalFree || uses(k)) {
+    if (KK == kInterior || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, scale_log2);
       softmax_exp<1, false>(xs, m_run, l_run, scale_log2, pk);
     }
@@ -1674,31 +1684,38 @@ __global__ __launch_bounds__(512, 1) void prefill_fused_kernel(const PrefillArgs
     lds_barrier();
   };
 
+  // tile k+1's kind decides its staging: corrected keys (interior tiles, and
+  // unmasked local tiles with a zero rotation), both kinds (edge) or the keys
+  // as cached (masked local tiles)
+  using KI = std::integral_constant<int, kInterior>;
+  using KE = std::integral_constant<int, kEdge>;
+  using KL = std::integral_constant<int, kLocal>;
   int k = 0;
-  for (; k + 1 < n_interior; ++k) tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kInterior>{});
+  for (; k + 1 < n_interior; ++k) tile(k, KI{}, KI{});
   if (k < n_interior) {
-    if (k + 1 < t_local) tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kEdge>{});
-    else tile(k, std::integral_constant<int, kInterior>{}, std::integral_constant<int, kLocal>{});
+    if (k + 1 < t_local) tile(k, KI{}, KE{});
+    else if (k + 1 < t_free) tile(k, KI{}, KI{});
+    else tile(k, KI{}, KL{});
     ++k;
   }
   for (; k < t_local; ++k) {
-    if (k + 1 < t_local) tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kEdge>{});
-    else tile(k, std::integral_constant<int, kEdge>{}, std::integral_constant<int, kLocal>{});
+    if (k + 1 < t_local) tile(k, KE{}, KE{});
+    else if (k + 1 < t_free) tile(k, KE{}, KI{});
+    else tile(k, KE{}, KL{});
   }
+  // from here on the query fragment is the base-RoPE one (the corrected one is dead)
   {
     u32x4 raw[8];
     load_qraw(raw);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(raw[kk]);
+    for (int kk = 0; kk < 8; ++kk) qg[kk] = as_bf16x8(raw[kk]);
   }
-  {
-    const int t_free = min(ntiles, max(k, (p0_wg + 1) / kBN));
-    for (; k < t_free; ++k) {
-      if (k + 1 < t_free) tile(k, std::integral_constant<int, kLocalFree>{}, std::integral_constant<int, kLocalFree>{});
-      else tile(k, std::integral_constant<int, kLocalFree>{}, std::integral_constant<int, kLocal>{});
-    }
+  for (; k + 1 < t_free; ++k) tile(k, KI{}, KI{});
+  if (k < t_free) {
+    tile(k, KI{}, KL{});
+    ++k;
   }
-  for (; k < ntiles; ++k) tile(k, std::integral_constant<int, kLocal>{}, std::integral_constant<int, kLocal>{});
+  for (; k < ntiles; ++k) tile(k, KL{}, KL{});
   // the V copies of the tiles staged past the last are still in flight: none
   // may land after the workgroup ends
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
