@@ -170,6 +170,23 @@ jl_status jl_bifocal_prefill_passes(const void* q, const void* k, const void* v,
                                     int64_t pretrained_window, int64_t local_window,
                                     double rope_base, float softmax_scale, void* stream);
 
+/* The merge in its literal form: the same three passes in one kernel sweep over
+ * shared LDS tiles, each with its own running maximum and normaliser, combined
+ * in the epilogue by their log-sum-exp weights with C subtracted (Abstract and
+ * ResearchPod summary, 2nd paragraph: the views are joined without counting the
+ * near keys twice):  Z = e_A + e_B - e_C,  O = (e_A O_A + e_B O_B - e_C O_C) / Z,
+ * e_X = exp(lse_X - max lse),  lse = max lse + ln Z.
+ * Same arguments, layouts and errors as jl_bifocal_prefill without q_pos (rows
+ * sit at n_kv - n_q + i):  out bf16 [B, n_q, Hq, D];  lse fp32 [B, Hq, n_q] or
+ * NULL.  It equals jl_bifocal_prefill up to rounding (that kernel folds the
+ * three passes into one softmax with a shared maximum); it runs the three
+ * passes for every g, including g == 1, and is slower.  For checking. */
+jl_status jl_bifocal_prefill_three_pass(const void* q, const void* k, const void* v, void* out,
+                                        float* lse, int32_t batch, int32_t n_q, int32_t n_kv,
+                                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                        int64_t pretrained_window, int64_t local_window,
+                                        double rope_base, float softmax_scale, void* stream);
+
 /* Bytes of device workspace jl_bifocal_decode / jl_plain_decode need for this
  * shape (an upper bound over every L and W).  0 for invalid sizes. */
 size_t jl_bifocal_decode_workspace_size(int32_t batch, int32_t n_kv, int32_t n_q_heads,

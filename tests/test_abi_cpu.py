@@ -100,6 +100,14 @@ def test_no_device_reports_device_error(lib):
     assert lib.jl_plain_prefill(FAKE, FAKE, FAKE, FAKE, None, FAKE + 1, 1, 8, 8, 1, 1, 128, 0.0, None) == INVALID
     assert lib.jl_bifocal_prefill_passes(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 1, 1, 128, 4, 2, 1e4, 0.0,
                                          None) == DEVICE
+    assert lib.jl_bifocal_prefill_three_pass(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 8, 1, 1, 128, 4, 2, 1e4, 0.0,
+                                             None) == DEVICE
+    assert lib.jl_bifocal_prefill_three_pass(FAKE, FAKE, FAKE, None, None, 1, 8, 8, 1, 1, 128, 4, 2, 1e4, 0.0,
+                                             None) == INVALID
+    assert lib.jl_bifocal_prefill_three_pass(FAKE, FAKE, FAKE, FAKE, FAKE + 4, 1, 8, 8, 1, 1, 128, 4, 2, 1e4, 0.0,
+                                             None) == INVALID
+    assert lib.jl_bifocal_prefill_three_pass(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 8, 1, 1, 128, 2, 4, 1e4, 0.0,
+                                             None) == INVALID  # W > L
     ws = lib.jl_bifocal_decode_workspace_size(1, 100, 4, 2, 128)
     assert lib.jl_bifocal_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 100, 4, 2, 128, 32, 8, 1e4, 0.0, FAKE, ws,
                                  None) == DEVICE

@@ -117,6 +117,39 @@ def test_three_passes_match_oracle_passes(case):
     assert_parity(merged, ref["out"], "merge of GPU passes")
 
 
+@pytest.mark.parametrize("case", [(130, 1, 2048, 2048, 1, 1, 512, 128, 1e4), (131, 1, 300, 300, 4, 2, 64, 40, 1e4),
+                                  (133, 2, 333, 333, 8, 2, 100, 37, 1e6), (134, 1, 64, 64, 2, 1, 64, 16, 1e4),
+                                  (135, 1, 90, 400, 4, 1, 128, 128, 1e4)])
+def test_three_pass_merge_in_kernel(case):
+    # The literal form of the merge: three passes, each with its own maximum and
+    # normaliser, combined by their lse weights in the kernel's epilogue.  Against
+    # the oracle's merged result, and against the oracle's merge of the same
+    # kernel's per-pass outputs, which it must equal up to the output's bf16
+    # rounding (half an ulp: 2^-8 relative) and fp32 rounding in the lse.
+    wid, b, n_q, n_kv, hq, hkv, big_l, w, base = case
+    qb, kb, vb = make_qkv(wid, b, n_q, n_kv, hq, hkv, 128)
+    q, k, v = to_device(qb), to_device(kb), to_device(vb)
+    print(f"case three-pass merge workload={wid} B={b} n_q={n_q} n_kv={n_kv} Hq={hq} Hkv={hkv} L={big_l} W={w}",
+          flush=True)
+    out = torch.empty_like(q)
+    lse = torch.empty((b, hq, n_q), dtype=torch.float32, device="cuda:0")
+    jl.jl_bifocal_prefill_three_pass(q, k, v, out, lse, big_l, w, base)
+    out_abc = torch.empty((3, b, n_q, hq, 128), dtype=torch.float32, device="cuda:0")
+    lse_abc = torch.empty((3, b, hq, n_q), dtype=torch.float32, device="cuda:0")
+    jl.jl_bifocal_prefill_passes(q, k, v, out_abc, lse_abc, big_l, w, base)
+    torch.cuda.synchronize()
+    got, got_lse = to_f64(out), lse.cpu().numpy().astype(np.float64)
+    ref = oracle.bifocal_three_pass(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb), big_l, w, base)
+    assert_parity(got, ref["out"], "three-pass merge")
+    assert_parity(got_lse, ref["lse"], "lse", max_tol=lse_tol(ref["g"]), mean_tol=LSE_MEAN_TOL)
+    o = out_abc.cpu().numpy().astype(np.float64)
+    ls = lse_abc.cpu().numpy().astype(np.float64)
+    merged, merged_lse = oracle.merge_passes(o[0], ls[0], o[1], ls[1], o[2], ls[2])
+    assert np.all(np.abs(got - merged) <= np.abs(merged) * 2.0 ** -8 * 1.01 + 1e-6), \
+        np.abs(got - merged).max()
+    assert np.abs(got_lse - merged_lse).max() <= 1e-4
+
+
 def test_deterministic_and_causal():
     wid, b, n_q, n_kv, hq, hkv, big_l, w, base = 140, 1, 1100, 1100, 4, 1, 300, 64, 1e4
     qb, kb, vb = make_qkv(wid, b, n_q, n_kv, hq, hkv, 128)

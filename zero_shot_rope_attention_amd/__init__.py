@@ -24,6 +24,7 @@ __all__ = [
     "jl_bifocal_prefill_ws",
     "jl_plain_prefill",
     "jl_bifocal_prefill_passes",
+    "jl_bifocal_prefill_three_pass",
     "jl_bifocal_decode_workspace_size",
     "jl_bifocal_decode",
     "jl_plain_decode",
@@ -64,6 +65,8 @@ _SIGNATURES = {
     "jl_plain_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "jl_bifocal_prefill_passes": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
                                          _f64, _f32, _vp]),
+    "jl_bifocal_prefill_three_pass": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                             _i64, _f64, _f32, _vp]),
     "jl_bifocal_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "jl_bifocal_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _f64, _f32,
                                  _vp, _sz, _vp]),
@@ -192,6 +195,17 @@ def jl_bifocal_prefill_passes(q, k, v, out_abc, lse_abc, pretrained_window, loca
     _check(load_library().jl_bifocal_prefill_passes(_ptr(q), _ptr(k), _ptr(v), _ptr(out_abc), _ptr(lse_abc), b, n_q,
                                                     n_kv, hq, hkv, d, int(pretrained_window), int(local_window),
                                                     float(rope_base), float(softmax_scale), _stream(stream)))
+
+
+def jl_bifocal_prefill_three_pass(q, k, v, out, lse, pretrained_window, local_window, rope_base, softmax_scale=0.0,
+                                  stream=None):
+    """The three passes merged by their lse weights in one kernel: out bf16 [B, n_q, Hq, D]; lse fp32 [B, Hq, n_q]
+    or None."""
+    b, n_q, hq, d = q.shape
+    n_kv, hkv = k.shape[1], k.shape[2]
+    _check(load_library().jl_bifocal_prefill_three_pass(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, n_q,
+                                                        n_kv, hq, hkv, d, int(pretrained_window), int(local_window),
+                                                        float(rope_base), float(softmax_scale), _stream(stream)))
 
 
 def jl_bifocal_decode_workspace_size(batch, n_kv, n_q_heads, n_kv_heads, head_dim=128) -> int:

@@ -209,6 +209,25 @@ jl_status jl_bifocal_prefill_passes(const void* q, const void* k, const void* v,
   return launched(jl::launch_prefill(jl::kModePasses, p, static_cast<hipStream_t>(stream)));
 }
 
+jl_status jl_bifocal_prefill_three_pass(const void* q, const void* k, const void* v, void* out, float* lse,
+                                        int32_t batch, int32_t n_q, int32_t n_kv, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t head_dim, int64_t pretrained_window,
+                                        int64_t local_window, double rope_base, float softmax_scale, void* stream) {
+  float scale;
+  const Shape s{batch, n_q, n_kv, n_q_heads, n_kv_heads, head_dim};
+  JL_TRY(prefill_common(q, k, v, s, softmax_scale, &scale));
+  JL_TRY(check_pointer(out, "out"));
+  JL_TRY(check_pointer(lse, "lse", true));
+  JL_TRY(check_windows(pretrained_window, local_window, rope_base));
+  JL_TRY(device_check());
+  const int64_t g = jl_group_factor(n_kv, pretrained_window);
+  const int32_t w = (int32_t)(local_window < n_kv ? local_window : n_kv);
+  // no per-pass buffers: the passes kernel writes the merged output and lse
+  jl::PrefillProblem p{q, k, v, out, lse, nullptr, nullptr, nullptr, batch, n_q, n_kv, n_q_heads, n_kv_heads,
+                       (int32_t)g, w, rope_base, scale};
+  return launched(jl::launch_prefill(jl::kModePasses, p, static_cast<hipStream_t>(stream)));
+}
+
 size_t jl_bifocal_prefill_workspace_size(int32_t batch, int32_t n_kv, int32_t n_kv_heads, int32_t head_dim) {
   if (batch < 1 || n_kv < 1 || n_kv_heads < 1 || head_dim != 128) return 0;
   const int64_t e = elements(batch, n_kv, n_kv_heads);

@@ -67,7 +67,7 @@ struct PrefillProblem {
   const void* v;
   void* out;        // bf16 [B, n_q, Hq, D]       (plain / bifocal)
   float* lse;       // fp32 [B, Hq, n_q] or null  (plain / bifocal)
-  float* out_abc;   // fp32 [3, B, n_q, Hq, D]    (passes)
+  float* out_abc;   // fp32 [3, B, n_q, Hq, D]    (passes; null: out/lse take the merged result)
   float* lse_abc;   // fp32 [3, B, Hq, n_q]       (passes)
   void* kg;         // bf16 [B, n_kv, Hkv, D] corrected keys (bifocal, precorrected)
   int32_t batch, n_q, n_kv, n_q_heads, n_kv_heads;

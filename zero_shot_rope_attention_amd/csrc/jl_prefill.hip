@@ -658,6 +658,45 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(const PrefillArgs a
 
   // ---- epilogue: lane holds row my_row, columns d = 32nb + 8(i/4) + 4h + (i%4) ----
   if (!row_ok) return;
+  if constexpr (MODE == kModePasses) {
+    if (!a.out_abc) {
+      // Merged output (no per-pass buffers): the inclusion-exclusion of the three
+      // passes A (local keys, base scores), B (causal keys, grouped scores) and C
+      // (local keys, grouped scores), each weighted by its own normaliser.  In
+      // log2 units lse_X = m_X tau log2(e) + log2 l_X; with M the largest lse,
+      // e_X = 2^(m_X tau log2(e) - M) scales pass X's unnormalised sums, so
+      //   Z = e_A l_A + e_B l_B - e_C l_C,  O = (e_A acc_A + e_B acc_B - e_C acc_C) / Z,
+      //   lse = (M + log2 Z) ln 2.
+      // Each l_X is the sum over the row's two lane halves (a cross-lane reduction).
+      float lt[NS], ml[NS], e[NS];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        lt[s] = half_sum(l_run[s]);
+        ml[s] = m_run[s] * a.scale_log2;
+        if (lt[s] > 0.0f) mx = fmaxf(mx, ml[s] + __builtin_log2f(lt[s]));
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) e[s] = lt[s] > 0.0f ? __builtin_amdgcn_exp2f(ml[s] - mx) : 0.0f;
+      const float z = __builtin_fmaf(e[0], lt[0], __builtin_fmaf(e[1], lt[1], -e[2] * lt[2]));
+      const float inv = 1.0f / z;
+      const float c0 = e[0] * inv, c1 = e[1] * inv, c2 = -e[2] * inv;
+      auto merged = [&](int nb, int i) {
+        return __builtin_fmaf(acc[0][nb][i], c0, __builtin_fmaf(acc[1][nb][i], c1, acc[2][nb][i] * c2));
+      };
+      uint16_t* o = a.out + (((int64_t)b * a.n_q + my_row) * a.hq + hq) * kD;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          u32x2 val = {pack_bf16(merged(nb, 4 * i4), merged(nb, 4 * i4 + 1)),
+                       pack_bf16(merged(nb, 4 * i4 + 2), merged(nb, 4 * i4 + 3))};
+          *reinterpret_cast<u32x2*>(o + 32 * nb + 8 * i4 + 4 * h) = val;
+        }
+      if (a.lse && h == 0) a.lse[((int64_t)b * a.hq + hq) * a.n_q + my_row] = (mx + __builtin_log2f(z)) * kLn2;
+      return;
+    }
+  }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const float lt = half_sum(l_run[s]);
