@@ -145,12 +145,32 @@ def cpu_baseline(qb, kb, vb, big_l, w, base, hq, hkv, n_rows, seed=0):
     dt = time.perf_counter() - t0
     flops = 4.0 * 128 * grp * float(np.sum(rows + 1))
     threads = os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS")
+    b = qb.shape[0]
+    # the whole prefill at the sample's rate (the oracle's cost grows with the causal pairs)
+    full_s = prefill_flops(b, s, hq) / (flops / dt)
+    # decode: the oracle's one-query call on the decode lengths, the query being the workload's
+    # row at position n - 1 and the cache its first n keys (every head)
+    dec = []
+    for n in [x for x in DECODE_LENGTHS if x <= s]:
+        qd = bf16_bits_to_f64(qb[:, n - 1:n])
+        kd = bf16_bits_to_f64(kb[:, :n])
+        vd = bf16_bits_to_f64(vb[:, :n])
+        t1 = time.perf_counter()
+        oracle.bifocal_decode(qd, kd, vd, big_l, w, base)
+        dd = time.perf_counter() - t1
+        kv_bytes = 2 * b * n * hkv * 128 * 2
+        dec.append({"n_kv": n, "seconds": round(dd, 4), "us_per_call": round(dd * 1e6, 1),
+                    "kv_GB_s": round(kv_bytes / dd / 1e9, 4)})
+        del qd, kd, vd
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads) if threads else os.cpu_count(),
             "kind": "oracle",
             "sample": f"{n_rows} random query rows x {grp} query heads (KV head 0) of the workload, "
                       f"fp64 numpy three-pass oracle, {dt:.1f} s; rate = algorithmic flops of those rows / time",
             "seconds": dt, "host_cpus": os.cpu_count(),
-            "pairs_per_s": grp * float(np.sum(rows + 1)) / dt}
+            "pairs_per_s": grp * float(np.sum(rows + 1)) / dt,
+            "extrapolated_full_prefill_s": round(full_s, 1),
+            "extrapolated_note": "the whole prefill (every row and head) at the sample's rate; not run",
+            "decode": dec}
 
 
 def bench_prefill_varlen(jl, torch, s, hq, hkv, big_l, w, base, args):
