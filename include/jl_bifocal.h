@@ -18,7 +18,7 @@
  *     recovered exactly; the merge and the rotation that moves cached vectors to
  *     their folded positions are computed inside the attention kernel.
  *   - seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap":
- *     the long-range factor is derived from the current sequence length s.
+ *     the long-range factor follows the length s of the sequence at hand.
  *
  * Definitions used by every entry point (head size D = 128):
  *   s      = n_kv, the number of keys in context (cache index == position).
@@ -452,7 +452,7 @@ jl_status jl_plain_prefill_positions(const void* q, const void* k, const void* v
                                      int32_t head_dim, float softmax_scale, void* stream);
 
 /* ---- A Qwen3-shaped attention layer ---------------------------------------
- * The method runs inside Qwen3 models of 1.7B, 4B and 8B parameters at up to 128K
+ * The method runs inside three Qwen3 sizes (1.7B, 4B, 8B) at up to 128K
  * tokens (seventnews.com, "Empirical results that challenge the status quo").
  * One attention layer of such a model, with the attention step bifocal or plain,
  * so that the attention's share of a layer can be measured:

@@ -21,8 +21,8 @@ cited by page and section:
   short inputs; the merge and the rotation to folded positions run inside the
   attention kernel.
 * seventnews.com, "How bifocal attention sidesteps the fixed-scaling trap": the
-  long-range factor is computed from the current sequence length s; the merge
-  combines the branches without double-counting.
+  long-range factor follows the length s of the sequence at hand; the merge
+  joins the branches so that no key is counted twice.
 
 * seventnews.com, "Empirical results that challenge the status quo": the method
   runs inside Qwen3 models (1.7B, 4B, 8B) at up to 128K; ``oracle.layer`` states

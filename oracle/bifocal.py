@@ -96,11 +96,11 @@ __all__ = [
 def group_factor(seq_len: int, pretrained_window: int) -> int:
     """Grouping factor g(s) by direct search.
 
-    ResearchPod summary, 2nd paragraph: the remote window uses the *smallest
-    integer grouping* that keeps remote rotation angles inside the pretrained
-    distribution.  seventnews.com, "How bifocal attention sidesteps the
-    fixed-scaling trap": the long-range factor is computed from the current
-    sequence length s.
+    ResearchPod summary, 2nd paragraph: far keys are grouped by the least
+    integer factor for which their rotation angles stay within what
+    pretraining covered.  seventnews.com, "How bifocal attention sidesteps the
+    fixed-scaling trap": the factor follows the length s of the sequence at
+    hand.
 
     Reading: a key or query at position ``p < s`` is aliased to ``p // g``;
     pretraining saw positions (and distances) ``0 .. L-1``, so ``g`` is the

@@ -3,8 +3,8 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg
 may use this module.  It shares no code, table or helper with the HIP library.
 
-The pages evaluate the method on the Qwen3 family at 1.7B, 4B and 8B with
-contexts up to 128K (seventnews.com, "Empirical results that challenge the status
+The pages test the method on three Qwen3 sizes (1.7B, 4B, 8B) at contexts of
+up to 128K (seventnews.com, "Empirical results that challenge the status
 quo"), and one of them describes the method's cost as a few extra matrix products
 per layer (news.ubos.tech, "How It Works in Practice"; a low-reliability page).
 This module states the attention layer those models run, with the bifocal
