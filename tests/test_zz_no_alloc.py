@@ -50,3 +50,46 @@ def test_noalloc_decode_matches_the_workspace_decode_twice():
 def test_noalloc_decode_plain_length_and_workload_shape():
     _both(902, 1, 3000, 16, 4, 4096, 512, 1e6)                                  # g = 1: the plain kernels
     _both(903, 1, 131072, 32, 8, 32768, 4096, 1e6)                              # the 128K decode
+
+
+def test_noalloc_decode_under_graph_capture():
+    # The callers this entry point is for: a HIP graph captures several decode
+    # calls (different caches, shared library array), and every replay -- with
+    # the program's own eager work and synchronisations between replays -- must
+    # give bit for bit the eager results.  The path records no memset.
+    b, hq, hkv, big_l, w, base = 1, 32, 8, 32768, 4096, 1e6
+    lengths = (65536, 40000, 131072, 32768)
+    caches = []
+    for i, n in enumerate(lengths):
+        qb, kb, vb = make_qkv(910 + i, b, 1, n, hq, hkv, 128)
+        caches.append((to_device(qb), to_device(kb), to_device(vb)))
+    print(f"no-alloc decode under graph capture: lengths {lengths}", flush=True)
+    eager = []
+    for q, k, v in caches:
+        o = torch.empty_like(q)
+        l_ = torch.empty((b, hq, 1), dtype=torch.float32, device="cuda:0")
+        jl.jl_bifocal_decode_noalloc(q, k, v, o, l_, big_l, w, base)
+        eager.append((o, l_))
+    torch.cuda.synchronize()
+    outs = [(torch.empty_like(q), torch.empty((b, hq, 1), dtype=torch.float32, device="cuda:0"))
+            for q, _, _ in caches]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for (q, k, v), (o, l_) in zip(caches, outs):
+                jl.jl_bifocal_decode_noalloc(q, k, v, o, l_, big_l, w, base)  # on the capturing stream
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o, l_ in outs:
+            o.zero_()
+            l_.zero_()
+        # eager work on the array between replays: the graph must not depend on what it held
+        q, k, v = caches[rep % len(caches)]
+        jl.jl_bifocal_decode_noalloc(q, k, v, torch.empty_like(q), None, big_l, w, base)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, l_), (eo, el) in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16), eo.view(torch.int16)), f"replay {rep}"
+            assert torch.equal(l_, el), f"replay {rep}"
