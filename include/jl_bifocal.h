@@ -180,7 +180,10 @@ jl_status jl_bifocal_prefill_passes(const void* q, const void* k, const void* v,
  * sit at n_kv - n_q + i):  out bf16 [B, n_q, Hq, D];  lse fp32 [B, Hq, n_q] or
  * NULL.  It equals jl_bifocal_prefill up to rounding (that kernel folds the
  * three passes into one softmax with a shared maximum); it runs the three
- * passes for every g, including g == 1, and is slower.  For checking. */
+ * passes for every g, including g == 1, and is slower.  Subtracting C cancels:
+ * where the near keys' grouped weight exceeds everything else by ~1e7, the
+ * literal form loses the difference to fp32 rounding, which the shared-maximum
+ * form never computes.  For checking. */
 jl_status jl_bifocal_prefill_three_pass(const void* q, const void* k, const void* v, void* out,
                                         float* lse, int32_t batch, int32_t n_q, int32_t n_kv,
                                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
