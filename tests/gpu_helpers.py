@@ -10,9 +10,10 @@ the bar is 1e-3.  With g > 1 two further errors enter:
   carries a relative error of RMS ~1.6e-3 (round to nearest with 8 significant
   bits), which moves a score tau * q^g . k^g by ~1.6e-3 * sqrt(2 D) / sqrt(D) =
   2.3e-3 RMS for N(0, 1) inputs at D = 128;
-- the single-kernel form sums the bf16-rounded probabilities (one instruction
-  per pair in the loop that kernel is bound by): the normaliser's relative error
-  is a weighted mean of roundings of at most 2^-8, RMS ~2.2e-3 at most.
+- both bifocal forms (single kernel and two-launch) sum the bf16-rounded
+  probabilities, the weights the P V product applies, so that each output is a
+  convex combination of value rows: the normaliser's relative error is a
+  weighted mean of roundings of at most 2^-8, RMS ~2.2e-3 at most.
 The lse moves by the softmax-weighted mean of these errors, RMS up to
 sqrt(2.3^2 + 2.2^2) e-3 * sqrt(sum_j p_j^2): 3.2e-3 only where one key holds all
 the weight, far less once the weight is spread over the W + 1 or more keys of a

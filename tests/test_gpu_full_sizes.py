@@ -86,3 +86,39 @@ def test_sweep_within_window_is_plain_bitwise(s):
     ref, _ = oracle.plain_causal_attention(bf16_bits_to_f64(qb[:, :, :8]), bf16_bits_to_f64(kb[:, :, :2]),
                                            bf16_bits_to_f64(vb[:, :, :2]), rows=rows)
     assert_parity(to_f64(out[:, rows, :8]), ref, f"sweep {s}")
+
+
+def test_batch_of_two_at_48k():
+    # Batch offsets at a full-size shape: two sequences of 48K (32/8 heads, g = 2), so
+    # that the second sequence's rows, keys and outputs sit past the first's 48K x 32
+    # heads; sampled rows of both sequences over every KV head, both prefill forms.
+    b, s, hq, hkv, big_l, w, base = 2, 49152, 32, 8, 32768, 4096, 1e6
+    g = oracle.group_factor(s, big_l)
+    qb, kb, vb = make_qkv(5, b, s, s, hq, hkv, 128)
+    q, k, v = to_device(qb), to_device(kb), to_device(vb)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(w - 4, w + 4), np.arange(s - 8, s),
+                                     rng.choice(s, 16, replace=False)]))
+    grp = hq // hkv
+    refs = []
+    for kvh in range(hkv):
+        heads = slice(kvh * grp, (kvh + 1) * grp)
+        refs.append(oracle.bifocal_three_pass(bf16_bits_to_f64(qb[:, :, heads]), bf16_bits_to_f64(kb[:, :, kvh:kvh + 1]),
+                                              bf16_bits_to_f64(vb[:, :, kvh:kvh + 1]), big_l, w, base, rows=rows))
+    ws = torch.empty(jl.jl_bifocal_prefill_workspace_size(b, s, hkv), dtype=torch.uint8, device="cuda:0")
+    for form in ("fused", "two_launch"):
+        print(f"batch 2 at 48K: form={form}, {len(rows)} rows x 2 sequences x {hkv} KV heads", flush=True)
+        out = torch.empty_like(q)
+        lse = torch.empty((b, hq, s), dtype=torch.float32, device="cuda:0")
+        if form == "fused":
+            jl.jl_bifocal_prefill(q, k, v, out, lse, big_l, w, base)
+        else:
+            jl.jl_bifocal_prefill_ws(q, k, v, out, lse, big_l, w, base, ws)
+        torch.cuda.synchronize()
+        got = to_f64(out[:, rows])
+        got_lse = lse[:, :, rows].cpu().numpy().astype(np.float64)
+        for kvh in range(hkv):
+            heads = slice(kvh * grp, (kvh + 1) * grp)
+            assert_parity(got[:, :, heads], refs[kvh]["out"], f"batch 2 {form} kv head {kvh}")
+            assert_parity(got_lse[:, heads], refs[kvh]["lse"], "lse", max_tol=lse_tol(g), mean_tol=LSE_MEAN_TOL)
+        del out, lse

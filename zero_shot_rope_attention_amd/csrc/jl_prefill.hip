@@ -1199,7 +1199,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
     // ---- V(k): softmax of tile k, staging ----
     if (kKind == kInterior || kKind == kLocalFree || uses(k)) {
       softmax_max<1>(xs, m_run, l_run, acc, a.scale_log2);
-      softmax_exp<1, true>(xs, m_run, l_run, a.scale_log2, pk);
+      // plain and sliding windows: fp32 sums (the lse carries fp32 rounding only).
+      // Bifocal on corrected keys: the sums of the bf16-rounded probabilities, the
+      // weights P V applies, as in the single kernel, so that every output is a
+      // convex combination of value rows (an fp32 sum against bf16 weights adds an
+      // error of up to 2^-8 |out|, which shows on rows with few keys)
+      softmax_exp<1, MODE != kModeBifocalPre>(xs, m_run, l_run, a.scale_log2, pk);
     }
     // the scores are dead once the probabilities exist: keep the staging after
     __builtin_amdgcn_sched_barrier(0);
