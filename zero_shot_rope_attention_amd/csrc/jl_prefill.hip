@@ -1205,6 +1205,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(const PrefillArgs a)
       // convex combination of value rows (an fp32 sum against bf16 weights adds an
       // error of up to 2^-8 |out|, which shows on rows with few keys)
       softmax_exp<1, MODE != kModeBifocalPre>(xs, m_run, l_run, a.scale_log2, pk);
+      if constexpr (MODE == kModeBifocalPre) {
+        // with only bf16 sums nothing in this phase consumes the probabilities,
+        // and the compiler would sink their exponentials into the next MFMA
+        // phase (measured ≈ 3% slower): they are formed here
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(pk[0][kb][i]));
+      }
     }
     // the scores are dead once the probabilities exist: keep the staging after
     __builtin_amdgcn_sched_barrier(0);
